@@ -1,0 +1,243 @@
+"""Benchmark: verified tree nodes per second for one DDTree round on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole round on one batch of synthetic input: ddtree_build
+(log-softmax + top-K + best-first tree + mask), ddtree_verify_attn (tree
+attention over the prefix KV) and ddtree_accept (target argmax + walk), all
+enqueued on the current HIP stream. Inputs are resident in HBM before the
+timed region; several copies rotate from step to step so that a step's
+reads come from HBM rather than from the 256 MB last-level cache.
+
+Prints one JSON line. value = sum over requests of (num_nodes - 1) per step
+divided by the time per step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from draft_tree_build_amd import api, synth  # noqa: E402
+
+METRIC = "verified tree nodes/sec (build+tree-attn+accept) and % HBM roofline, 1 GPU"
+DEFAULT_WORKLOAD = "L16_V32000_K8_N64_P2048"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+KERNEL_SOURCES = {
+    "build": "draft_tree_build_amd/csrc/k_build.hip",
+    "verify": "draft_tree_build_amd/csrc/k_attn.hip",
+    "accept": "draft_tree_build_amd/csrc/k_accept.hip",
+}
+KERNEL_NAMES = {"build": "k_build", "verify": "k_attn_mfma", "accept": "k_argmax_walk"}
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w, prefix_lens, num_nodes, depths, esize):
+    """Bytes (and flops) each stage must move per step, by its definition."""
+    B, L, V, K, T = w.batch, w.L, w.V, w.K, w.T
+    W = (T + 63) // 64
+    build_bytes = B * L * V * esize + B * L * K * 8 + B * T * (4 * 4 + W * 8)
+    P = [int(p) for p in prefix_lens]
+    kv_rows = sum(P) + B * T
+    verify_bytes = kv_rows * w.Hkv * w.D * esize * 2 + B * T * w.Hq * w.D * esize * 2 + B * T * W * 8
+    # QK^T and PV over the prefix, plus each node's ancestors (depth + 1 keys)
+    anc = sum(int(depths[b][i]) + 1 for b in range(B) for i in range(int(num_nodes[b])))
+    verify_flops = 4.0 * w.Hq * w.D * sum(T * p for p in P)
+    verify_flops += 4.0 * w.Hq * w.D * anc
+    accept_bytes = sum(int(n) for n in num_nodes) * V * esize
+    return dict(build_bytes=build_bytes, verify_bytes=verify_bytes, verify_flops=verify_flops,
+                accept_bytes=accept_bytes)
+
+
+def source_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload, stage):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload, {}).get(stage)
+    if not ent or ent.get("source_sha") != source_hash(KERNEL_SOURCES[stage]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, nodes_per_step, budget_s):
+    """The oracle, single-threaded, on whole rounds of the same workload."""
+    import numpy as np
+    import oracle
+    x, roots, q, k, v, P, offs, tl = inputs
+    tau = w.taus[0]
+    sel = [(b, i, h) for b in range(w.batch) for i in range(w.T) for h in range(w.Hq)]
+    rounds, t0 = 0, time.perf_counter()
+    while True:
+        tree = oracle.build_tree(x, roots, w.K, w.N, tau)
+        oracle.attn_rows(q, k, v, offs, P, tree["num_nodes"], tree["mask"], w.T, w.Hq, w.Hkv, w.D,
+                         1.0 / math.sqrt(w.D), sel)
+        oracle.accept(tl, None, tree["tokens"], tree["parents"], tree["num_nodes"], w.L)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=nodes_per_step * rounds / el, unit="nodes/s", cores=1, kind="oracle",
+                sample="%d whole round(s) of %s (build, attention of all %d query rows, accept), "
+                       "single thread, %.1f s" % (rounds, w.name, len(sel), el))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(synth.WORKLOADS))
+    ap.add_argument("--rotate-mb", type=int, default=768,
+                    help="rotate input copies until their total exceeds this (0: one copy)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(2)
+    api.lib()  # fail loudly if the library is not built
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    tau = w.taus[0]
+    log("workload %s: generating inputs" % w.name)
+    x_cpu, _ = synth.drafter_logits(w)
+    roots_cpu = synth.root_tokens(w)
+    P_cpu = synth.prefix_lengths(w)
+    offs_cpu = synth.kv_offsets(P_cpu, w.T)
+    q_cpu, k_cpu, v_cpu = synth.qkv(w, P_cpu)
+    tl_cpu = synth.target_logits(w)
+    esize = 2 if w.dtype == "bf16" else 4
+    step_bytes = sum(t.numel() * t.element_size() for t in (x_cpu, q_cpu, k_cpu, v_cpu, tl_cpu))
+    R = 1
+    if args.rotate_mb > 0:
+        R = max(1, min(64, math.ceil(args.rotate_mb * 2**20 / step_bytes)))
+        free = torch.cuda.mem_get_info(dev)[0]
+        R = max(1, min(R, int(0.5 * free // step_bytes)))
+    log("%d input cop%s of %.1f MB" % (R, "y" if R == 1 else "ies", step_bytes / 1e6))
+    copies = []
+    for _ in range(R):
+        copies.append(tuple(t.to(dev) for t in (x_cpu, q_cpu, k_cpu, v_cpu, tl_cpu)))
+    roots = roots_cpu.to(dev)
+    P = P_cpu.to(dev)
+    offs = offs_cpu.to(dev)
+    rnd = api.Round(w.batch, w.L, w.V, w.K, w.N, dev, w.Hq, w.Hkv, w.D, int(w.prefix[1]),
+                    dtype=w.torch_dtype)
+
+    def step(i, ev=None):
+        x, q, k, v, tl = copies[i % R]
+        if ev is not None:
+            ev[0].record()
+        rnd.build(x, roots, tau)
+        if ev is not None:
+            ev[1].record()
+        rnd.verify(q, k, v, offs, P)
+        if ev is not None:
+            ev[2].record()
+        rnd.accept(tl)
+        if ev is not None:
+            ev[3].record()
+
+    log("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    num_nodes = rnd.num_nodes.cpu()
+    nodes_per_step = int((num_nodes - 1).sum())
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {"build": 0.0, "verify": 0.0, "accept": 0.0}
+    for ev in evs:
+        stage_ms["build"] += ev[0].elapsed_time(ev[1])
+        stage_ms["verify"] += ev[1].elapsed_time(ev[2])
+        stage_ms["accept"] += ev[2].elapsed_time(ev[3])
+    stage_us = {k: v * 1e3 / args.steps for k, v in stage_ms.items()}
+    value = nodes_per_step / (ms_per_step * 1e-3)
+    log("ms/step %.4f  stages(us) %s" % (ms_per_step, {k: round(v, 2) for k, v in stage_us.items()}))
+
+    if args.copy_probe:
+        a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    work = algorithmic_work(w, P_cpu.tolist(), num_nodes.tolist(), rnd.depths.cpu().tolist(), esize)
+    dom = max(stage_us, key=stage_us.get)
+    t_s = stage_us[dom] * 1e-6
+    if dom == "verify":
+        t_mem = work["verify_bytes"] / (HBM_PEAK_GBS * 1e9)
+        t_mma = work["verify_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+        if t_mma > t_mem:
+            achieved, peak, unit, bound = work["verify_flops"] / t_s / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s", "mfma"
+        else:
+            achieved, peak, unit, bound = work["verify_bytes"] / t_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    else:
+        nbytes = work[dom + "_bytes"]
+        achieved, peak, unit, bound = nbytes / t_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
+                    frac=round(achieved / peak, 5), traffic=load_traffic(w.name, dom),
+                    kernel=KERNEL_NAMES[dom], stage=dom, avg_launch_us=round(stage_us[dom], 3))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (%.0f s budget)" % args.cpu_seconds)
+        inputs = (x_cpu, roots_cpu, q_cpu, k_cpu, v_cpu, P_cpu.numpy(), offs_cpu.numpy(), tl_cpu)
+        cpu = cpu_baseline(w, inputs, nodes_per_step, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; drafter/target logits ~N(0,sigma) with planted peaks, "
+                "Q/K/V ~N(0,1))",
+        "config": {"workload": w.name, "batch": w.batch, "L": w.L, "V": w.V, "K": w.K, "N": w.N,
+                   "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "draft_temp": tau, "input_copies": R},
+        "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

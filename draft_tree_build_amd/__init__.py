@@ -5,3 +5,10 @@ The work runs in hand-written HIP kernels behind the C ABI declared in
 binding over it (argument marshalling only) plus the seeded input
 generators in ``synth``.
 """
+
+from . import synth  # noqa: F401  (seeded inputs; no method arithmetic)
+from .api import (  # noqa: F401
+    DDTreeError, Round, ddtree_accept, ddtree_accept_workspace_size, ddtree_build,
+    ddtree_build_workspace_size, ddtree_mask, ddtree_verify_attn, ddtree_verify_workspace_size,
+    lib, new_workspace, strerror, version,
+)

@@ -1,0 +1,190 @@
+// C ABI of the DDTree hot path (declared in include/ddtree.h): argument
+// validation, workspace layout and launches. Every check here runs before
+// anything is enqueued, so a rejected call has no effect on the device.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/ddtree.h"
+#include "ddtree_internal.h"
+
+using namespace ddt;
+
+namespace {
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP; }
+
+inline bool dtype_ok(int dt) { return dt == DDTREE_BF16 || dt == DDTREE_F32; }
+
+}  // namespace
+
+extern "C" {
+
+int ddtree_version(void) { return DDTREE_VERSION; }
+
+const char* ddtree_strerror(int status) {
+  switch (status) {
+    case DDTREE_OK: return "ok";
+    case DDTREE_ERR_ARG: return "invalid argument (null pointer, size or range)";
+    case DDTREE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case DDTREE_ERR_WORKSPACE: return "workspace missing or too small";
+    case DDTREE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t ddtree_build_workspace_size(int batch, int L, int V, int K, int N) {
+  (void)V;
+  (void)N;
+  if (batch < 1 || L < 1 || K < 1) return 0;
+  return build_workspace_bytes(batch, L, K);
+}
+
+int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens, int batch,
+                 int L, int V, int K, int N, float draft_temp, int32_t* tokens,
+                 int32_t* parents, int32_t* depths, float* scores, int32_t* num_nodes,
+                 uint64_t* mask, int32_t* topk_tokens, float* topk_logprobs,
+                 int32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !root_tokens || !tokens || !parents || !depths || !scores || !num_nodes)
+    return DDTREE_ERR_ARG;
+  if (batch < 1 || L < 1 || V < 1 || K < 1 || N < 1) return DDTREE_ERR_ARG;
+  if (K > V) return DDTREE_ERR_ARG;
+  if (!(draft_temp >= 0.0f) || isinf(draft_temp)) return DDTREE_ERR_ARG;
+  if (!dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
+  if (L > DDTREE_MAX_L || K > DDTREE_MAX_K || N > DDTREE_MAX_N || V > DDTREE_MAX_V)
+    return DDTREE_ERR_UNSUPPORTED;
+  if ((long long)batch * L > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  const size_t need = build_workspace_bytes(batch, L, K);
+  if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
+
+  BuildArgs a{};
+  a.logits = logits;
+  a.dtype = dt;
+  a.root_tokens = root_tokens;
+  a.batch = batch;
+  a.L = L;
+  a.V = V;
+  a.K = K;
+  a.N = N;
+  if (draft_temp == 0.0f) {
+    a.mode = 2;
+    a.inv_tau = 1.0f;
+  } else {
+    a.inv_tau = 1.0f / draft_temp;
+    a.mode = (a.inv_tau == 1.0f) ? 0 : 1;
+  }
+  a.tokens = tokens;
+  a.parents = parents;
+  a.depths = depths;
+  a.scores = scores;
+  a.num_nodes = num_nodes;
+  a.mask = mask;
+  a.status = status_flags;
+  int32_t *ws_tok, *ws_flags, *ws_cnt;
+  float* ws_lp;
+  build_carve(workspace, batch, L, K, &ws_tok, &ws_lp, &ws_flags, &ws_cnt);
+  a.topk_tok = topk_tokens ? topk_tokens : ws_tok;
+  a.topk_lp = topk_logprobs ? topk_logprobs : ws_lp;
+  a.row_flags = ws_flags;
+  a.counters = ws_cnt;
+  return hip_status(launch_build(a, static_cast<hipStream_t>(stream)));
+}
+
+int ddtree_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,
+                uint64_t* mask, void* stream) {
+  if (!parents || !num_nodes || !mask) return DDTREE_ERR_ARG;
+  if (batch < 1 || T < 1) return DDTREE_ERR_ARG;
+  if (T > DDTREE_MAX_N + 1) return DDTREE_ERR_UNSUPPORTED;
+  return hip_status(launch_mask(parents, num_nodes, batch, T, mask,
+                                static_cast<hipStream_t>(stream)));
+}
+
+size_t ddtree_verify_workspace_size(ddtree_dtype dt, int batch, int T, int Hq, int Hkv, int D,
+                                    int max_prefix_len) {
+  if (batch < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_prefix_len < 0) return 0;
+  if (Hq % Hkv != 0) return 0;
+  return attn_workspace_bytes(dt, batch, T, Hq, Hkv, D, max_prefix_len);
+}
+
+int ddtree_verify_attn(const void* q, const void* k, const void* v, ddtree_dtype dt,
+                       const int64_t* kv_offsets, const int32_t* prefix_lens,
+                       const int32_t* num_nodes, const uint64_t* mask, int batch, int T, int Hq,
+                       int Hkv, int D, int max_prefix_len, int64_t total_rows,
+                       float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!q || !k || !v || !kv_offsets || !prefix_lens || !num_nodes || !mask || !out)
+    return DDTREE_ERR_ARG;
+  if (batch < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_prefix_len < 0 || total_rows < 1)
+    return DDTREE_ERR_ARG;
+  if (Hq % Hkv != 0) return DDTREE_ERR_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return DDTREE_ERR_ARG;
+  if (!dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
+  if (T > DDTREE_MAX_N + 1) return DDTREE_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128) return DDTREE_ERR_UNSUPPORTED;
+  if (dt == DDTREE_BF16 && D != 128) return DDTREE_ERR_UNSUPPORTED;
+  if ((long long)batch * T * Hq > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  const size_t need = attn_workspace_bytes(dt, batch, T, Hq, Hkv, D, max_prefix_len);
+  if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dtype = dt;
+  a.kv_offsets = kv_offsets;
+  a.prefix_lens = prefix_lens;
+  a.num_nodes = num_nodes;
+  a.mask = mask;
+  a.batch = batch;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.max_prefix_len = max_prefix_len;
+  a.total_rows = total_rows;
+  a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)D);
+  a.out = out;
+  return hip_status(launch_attn(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t ddtree_accept_workspace_size(int batch, int T) {
+  if (batch < 1 || T < 1) return 0;
+  return accept_workspace_bytes(batch, T);
+}
+
+int ddtree_accept(const void* target_logits, ddtree_dtype dt, const int32_t* target_ids,
+                  const int32_t* tokens, const int32_t* parents, const int32_t* num_nodes,
+                  int batch, int T, int V, int L, int32_t* accepted, int32_t* accepted_nodes,
+                  int32_t* accept_len, int32_t* bonus, int32_t* target_argmax, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!tokens || !parents || !num_nodes || !accepted || !accept_len || !bonus)
+    return DDTREE_ERR_ARG;
+  if (!target_logits && !target_ids) return DDTREE_ERR_ARG;
+  if (batch < 1 || T < 1 || L < 1) return DDTREE_ERR_ARG;
+  if (target_logits && V < 1) return DDTREE_ERR_ARG;
+  if (target_logits && !dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
+  if (T > DDTREE_MAX_N + 1 || L > DDTREE_MAX_L) return DDTREE_ERR_UNSUPPORTED;
+  if ((long long)batch * T > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  const size_t need = accept_workspace_bytes(batch, T);
+  if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
+  AcceptArgs a{};
+  a.target_logits = target_logits;
+  a.dtype = dt;
+  a.target_ids = target_ids;
+  a.tokens = tokens;
+  a.parents = parents;
+  a.num_nodes = num_nodes;
+  a.batch = batch;
+  a.T = T;
+  a.V = V;
+  a.L = L;
+  a.accepted = accepted;
+  a.accepted_nodes = accepted_nodes;
+  a.accept_len = accept_len;
+  a.bonus = bonus;
+  int32_t *ws_tgt, *ws_cnt;
+  accept_carve(workspace, batch, T, &ws_tgt, &ws_cnt);
+  a.target_argmax = target_argmax ? target_argmax : ws_tgt;
+  a.counters = ws_cnt;
+  return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

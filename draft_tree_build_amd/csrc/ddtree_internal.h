@@ -1,0 +1,80 @@
+// Host-side launch interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ddt {
+
+// ---------------------------------------------------------------- build
+struct BuildArgs {
+  const void* logits;       // [batch, L, V]
+  int dtype;                // 0 bf16, 1 f32
+  const int32_t* root_tokens;
+  int batch, L, V, K, N;
+  int mode;                 // 0: tau == 1, 1: tau > 0 (scale by inv_tau), 2: tau == 0 (argmax)
+  float inv_tau;
+  int32_t* tokens;
+  int32_t* parents;
+  int32_t* depths;
+  float* scores;
+  int32_t* num_nodes;
+  uint64_t* mask;           // may be null
+  int32_t* topk_tok;        // [batch, L, K] (caller output or workspace)
+  float* topk_lp;
+  int32_t* status;          // may be null
+  int32_t* row_flags;       // workspace [batch, L]
+  int32_t* counters;        // workspace [batch], zero between calls
+};
+size_t build_workspace_bytes(int batch, int L, int K);
+void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** topk_lp,
+                 int32_t** row_flags, int32_t** counters);
+hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
+
+hipError_t launch_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,
+                       uint64_t* mask, hipStream_t stream);
+
+// ---------------------------------------------------------------- verify
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int dtype;
+  const int64_t* kv_offsets;
+  const int32_t* prefix_lens;
+  const int32_t* num_nodes;
+  const uint64_t* mask;
+  int batch, T, Hq, Hkv, D;
+  int max_prefix_len;
+  int64_t total_rows;
+  float scale;
+  void* out;
+};
+size_t attn_workspace_bytes(int dtype, int batch, int T, int Hq, int Hkv, int D,
+                            int max_prefix_len);
+hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t stream);
+
+// ---------------------------------------------------------------- accept
+struct AcceptArgs {
+  const void* target_logits;  // may be null
+  int dtype;
+  const int32_t* target_ids;  // used when target_logits is null
+  const int32_t* tokens;
+  const int32_t* parents;
+  const int32_t* num_nodes;
+  int batch, T, V, L;
+  int32_t* accepted;
+  int32_t* accepted_nodes;    // may be null
+  int32_t* accept_len;
+  int32_t* bonus;
+  int32_t* target_argmax;     // caller output or workspace
+  int32_t* counters;          // workspace [batch]
+};
+size_t accept_workspace_bytes(int batch, int T);
+void accept_carve(void* ws, int batch, int T, int32_t** tgt, int32_t** counters);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace ddt

@@ -1,0 +1,611 @@
+// Draft-tree build on gfx950: per-position log-softmax + top-K, best-first
+// tree, ancestor bitmask -- one kernel launch.
+//
+// Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees"
+// (Ringel, Romano), summary page, cited as [BDDT <section>].
+//
+// Grid: one workgroup per drafter row (request b, position i). Each workgroup
+// streams its row from HBM once (kept in registers when it fits), computes the
+// row maximum, the K best tokens and the exact fixed-point softmax
+// normaliser, and writes the K candidates with their log-probabilities. The
+// last workgroup of a request to finish (arrival counter in the workspace)
+// then builds that request's tree with one wavefront and writes the tree
+// arrays and the ancestor mask. No host round trip, no second launch.
+#include "ddtree_device.h"
+#include "ddtree_internal.h"
+
+namespace ddt {
+namespace {
+
+constexpr int kCandMax = 2048;   // candidate buffer for the top-K sort (LDS)
+constexpr int kSlots = 17;       // frontier slots per lane: ceil((1024 + 1) / 64)
+constexpr uint64_t kEmpty = ~0ull;
+constexpr int kMaxLK = 64 * 32;
+constexpr int kMaxT = 1025;
+
+struct RowShared {
+  uint64_t cand[kCandMax];
+  uint32_t gmax[64];
+};
+struct TreeShared {
+  int32_t tok[kMaxLK];
+  float lp[kMaxLK];
+  int32_t ntok[kMaxT];
+  int32_t npar[kMaxT];
+  int32_t ndep[kMaxT];
+  float nscore[kMaxT];
+};
+union BuildShared {
+  RowShared row;
+  TreeShared tree;
+};
+
+// ------------------------------------------------------------------ input views
+template <typename IN_T>
+struct Elem;
+template <>
+struct Elem<uint16_t> {  // bfloat16 bits
+  static constexpr int kPerVec = 8;
+  __device__ __forceinline__ static float scalar(const uint16_t* p, int i) { return bf16_to_float(p[i]); }
+  template <class F>
+  __device__ __forceinline__ static void unpack(const uint4& r, int base, F&& f) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f(base + 2 * j, __uint_as_float(w[j] << 16));
+      f(base + 2 * j + 1, __uint_as_float(w[j] & 0xFFFF0000u));
+    }
+  }
+};
+template <>
+struct Elem<float> {
+  static constexpr int kPerVec = 4;
+  __device__ __forceinline__ static float scalar(const float* p, int i) { return p[i]; }
+  template <class F>
+  __device__ __forceinline__ static void unpack(const uint4& r, int base, F&& f) {
+    f(base + 0, __uint_as_float(r.x));
+    f(base + 1, __uint_as_float(r.y));
+    f(base + 2, __uint_as_float(r.z));
+    f(base + 3, __uint_as_float(r.w));
+  }
+};
+
+// A drafter row as seen by one thread. CH > 0: the thread's 16-byte vectors
+// c*BLOCK + tid (c < CH) are held in registers; CH == 0: vectors re-read per
+// pass; CH < 0: scalar elements (any alignment). Elements are visited in
+// increasing token id per thread; chunk c covers ids in a contiguous range.
+template <typename IN_T, int BLOCK, int CH>
+struct RowView {
+  static constexpr int EPV = Elem<IN_T>::kPerVec;
+  const IN_T* row;
+  int V;
+  int nvec;
+  uint4 reg[CH > 0 ? CH : 1];
+
+  __device__ __forceinline__ void load(int tid) {
+    if constexpr (CH > 0) {
+      const uint4* p = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        // clamped, unconditional loads: all CH requests are in flight at once;
+        // vectors past the row end are never visited
+        const int vi = min(c * BLOCK + tid, nvec - 1);
+        reg[c] = p[vi];
+      }
+    }
+  }
+  // Opaque register barrier between passes: keeps the compiler from caching
+  // unpacked values of one pass for the next (which would hold every element
+  // of the row in fp32 and spill).
+  __device__ __forceinline__ void fence() {
+    if constexpr (CH > 0) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        asm volatile("" : "+v"(reg[c].x), "+v"(reg[c].y), "+v"(reg[c].z), "+v"(reg[c].w));
+    }
+  }
+  __device__ __forceinline__ int num_chunks() const {
+    if constexpr (CH < 0) return (V + BLOCK - 1) / BLOCK;
+    return (nvec + BLOCK - 1) / BLOCK;
+  }
+  // Chunk c straight from memory (used by the rare exact fallback only, so
+  // that the register copy is never indexed by a runtime chunk number).
+  template <class F>
+  __device__ __forceinline__ void visit_chunk(int c, int tid, F&& f) const {
+    if constexpr (CH >= 0) {
+      int vi = c * BLOCK + tid;
+      if (vi < nvec) Elem<IN_T>::unpack(reinterpret_cast<const uint4*>(row)[vi], vi * EPV, f);
+    } else {
+      int v = c * BLOCK + tid;
+      if (v < V) f(v, Elem<IN_T>::scalar(row, v));
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void visit_mem(int tid, F&& f) const {
+    const int nc = num_chunks();
+    for (int c = 0; c < nc; ++c) visit_chunk(c, tid, f);
+  }
+  template <class F>
+  __device__ __forceinline__ void visit(int tid, F&& f) const {
+    if constexpr (CH > 0) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        int vi = c * BLOCK + tid;
+        if (vi < nvec) Elem<IN_T>::unpack(reg[c], vi * EPV, f);
+      }
+    } else {
+      const int nc = num_chunks();
+      for (int c = 0; c < nc; ++c) visit_chunk(c, tid, f);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ block helpers
+template <int BLOCK>
+__device__ float block_max(float v, float* scratch) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int w = 1; w < BLOCK / 64; ++w) r = fmaxf(r, scratch[w]);
+  return r;
+}
+template <int BLOCK>
+__device__ int block_or(int v, int* scratch) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  int r = 0;
+  for (int w = 0; w < BLOCK / 64; ++w) r |= scratch[w];
+  return r;
+}
+template <int BLOCK>
+__device__ int block_sum(int v, int* scratch) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  int r = 0;
+  for (int w = 0; w < BLOCK / 64; ++w) r += scratch[w];
+  return r;
+}
+template <int BLOCK>
+__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* scratch) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  uint64_t r = 0;
+  for (int w = 0; w < BLOCK / 64; ++w) r += scratch[w];
+  return r;
+}
+// Exclusive prefix sum over the block (thread order); returns the block total.
+template <int BLOCK>
+__device__ int block_exclusive_scan(int v, int* excl, int* scratch) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int inc = wave_inclusive_scan(v, lane);
+  __syncthreads();
+  if (lane == 63) scratch[wid] = inc;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < BLOCK / 64; ++w) {
+    int s = scratch[w];
+    if (w < wid) before += s;
+    total += s;
+  }
+  *excl = before + inc - v;
+  return total;
+}
+
+// Bitonic sort of s[0..P) into descending order; P a power of two.
+template <int BLOCK>
+__device__ void bitonic_desc(uint64_t* s, int P) {
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < (P >> 1); i += BLOCK) {
+        int a = 2 * i - (i & (j - 1));
+        int b = a + j;
+        bool desc = (a & k) == 0;
+        uint64_t x = s[a], y = s[b];
+        if ((x < y) == desc) {
+          s[a] = y;
+          s[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Candidate word for the top-K sort: larger = better = (x desc, id asc).
+__device__ __forceinline__ uint64_t cand_word(uint32_t key, int id) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+// ------------------------------------------------------------------ tree keys
+// Frontier key, smaller = popped first: score desc, depth, parent, rank asc.
+__device__ __forceinline__ uint64_t tree_key(float score, int depth, int parent, int rank) {
+  uint32_t hi = ~float_order(score);
+  uint32_t lo = ((uint32_t)depth << 25) | ((uint32_t)parent << 14) | ((uint32_t)rank << 9);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Best-first tree of one request, run by one wavefront  [BDDT §4.3, App. A].
+// Every popped node p keeps exactly one pending candidate, its next
+// unpopped child; it lives in register slot p/64 of lane p%64. A pop is a
+// wave-wide minimum over those keys; the popped candidate (parent p, depth d,
+// rank r) becomes node n, p's slot advances to rank r+1 (next sibling) and
+// n's slot takes n's best child. Returns num_nodes (root included).
+__device__ int tree_wave(TreeShared& sh, int L, int K, int N, int root_token) {
+  const int lane = threadIdx.x & 63;
+  const int S = (N + 1 + 63) >> 6;
+  uint64_t fk[kSlots];
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) fk[s] = kEmpty;
+  if (lane == 0) {
+    sh.ntok[0] = root_token;
+    sh.npar[0] = -1;
+    sh.ndep[0] = 0;
+    sh.nscore[0] = 0.0f;
+    fk[0] = tree_key(0.0f + sh.lp[0], 1, 0, 0);
+  }
+  int n = 1;
+  for (; n <= N; ++n) {
+    uint64_t lb = fk[0];
+#pragma unroll
+    for (int s = 1; s < kSlots; ++s)
+      if (s < S) lb = fk[s] < lb ? fk[s] : lb;
+    const uint64_t best = wave_min(lb);
+    if (best == kEmpty) break;
+    const uint32_t hi = (uint32_t)(best >> 32), lo = (uint32_t)best;
+    const float score = order_to_float(~hi);
+    const int d = (int)(lo >> 25);
+    const int p = (int)((lo >> 14) & 0x7FFu);
+    const int r = (int)((lo >> 9) & 31u);
+    const int tok = sh.tok[(d - 1) * K + r];
+    const float score_p = sh.nscore[p];
+    uint64_t kp = kEmpty, kn = kEmpty;
+    if (r + 1 < K) kp = tree_key(score_p + sh.lp[(d - 1) * K + r + 1], d, p, r + 1);
+    if (d + 1 <= L) kn = tree_key(score + sh.lp[d * K], d + 1, n, 0);
+    if (lane == 0) {
+      sh.ntok[n] = tok;
+      sh.npar[n] = p;
+      sh.ndep[n] = d;
+      sh.nscore[n] = score;
+    }
+    const int ps = p >> 6, pl = p & 63, ns = n >> 6, nl = n & 63;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      if (s == ps && lane == pl) fk[s] = kp;
+      if (s == ns && lane == nl) fk[s] = kn;
+    }
+  }
+  return n;
+}
+
+// ------------------------------------------------------------------ the kernel
+template <typename IN_T, int BLOCK, int CH, bool GENERAL>
+__global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
+  __shared__ BuildShared sm;
+  __shared__ float red_f[16];
+  __shared__ int red_i[16];
+  __shared__ uint64_t red_u[16];
+  __shared__ int s_cnt;
+  __shared__ uint32_t s_t0;
+  __shared__ float s_lse;
+  __shared__ int s_last;
+  __shared__ int s_nn;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r = blockIdx.x;
+  const int b = r / a.L;
+  const int K = a.K;
+  const int mode = GENERAL ? a.mode : 0;
+  const float inv_tau = a.inv_tau;
+
+  RowView<IN_T, BLOCK, CH> view;
+  view.row = reinterpret_cast<const IN_T*>(a.logits) + (size_t)r * a.V;
+  view.V = a.V;
+  view.nvec = a.V / RowView<IN_T, BLOCK, CH>::EPV;
+  view.load(tid);
+
+  auto xval = [&](float raw) __attribute__((always_inline)) -> float {  // ranking value before sanitising
+    float x = raw;
+    if (GENERAL && mode == 1) x = x * inv_tau;
+    return x;
+  };
+
+  // ---- pass 1: row maximum, non-finite flag, per-thread maximum key
+  float tmax = -INFINITY;
+  int tflag = 0;
+  bool has = false;
+  view.visit(tid, [&](int, float raw) __attribute__((always_inline)) {
+    float x = xval(raw);
+    bool bad = (x != x) || (x == INFINITY);
+    tflag |= bad ? 1 : 0;
+    x = bad ? -INFINITY : x;
+    tmax = fmaxf(tmax, x);
+    has = true;
+  });
+  const float m = block_max<BLOCK>(tmax, red_f);
+  int flags = block_or<BLOCK>(tflag, red_i);
+  if (m == -INFINITY) flags |= 2;
+
+  // ---- a lower bound t0 for the K-th largest key: the K-th largest of 64
+  //      group maxima (each is a distinct element of the row)
+  uint32_t tkey = has ? float_order(tmax) : 0u;
+  constexpr int G = BLOCK / 64;
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) {
+    uint32_t w = __shfl_xor(tkey, o, 64);
+    tkey = w > tkey ? w : tkey;
+  }
+  if ((tid % G) == 0) sm.row.gmax[tid / G] = tkey;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t v = sm.row.gmax[lane];
+    for (int k = 2; k <= 64; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint32_t o = __shfl_xor(v, j, 64);
+        bool desc = (lane & k) == 0;
+        bool low = (lane & j) == 0;
+        v = (low == desc) ? (o > v ? o : v) : (o < v ? o : v);
+      }
+    }
+    uint32_t t0 = __shfl(v, K - 1, 64);
+    if (lane == 0) s_t0 = t0;
+  }
+  __syncthreads();
+  const uint32_t t0 = s_t0;
+
+  auto key_of = [&](float raw) __attribute__((always_inline)) -> uint32_t {
+    float x = xval(raw);
+    x = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
+    return float_order(x);
+  };
+
+  // ---- pass 2, fused: candidates (every element with key >= t0) and the
+  //      exact fixed-point normaliser S = sum_v rint(2^44 E(x_v - m))
+  double acc = 0.0;
+  const bool finite_m = m != -INFINITY;
+  view.fence();
+  view.visit(tid, [&](int id, float raw) __attribute__((always_inline)) {
+    const float x = xval(raw);
+    const float xs = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
+    const uint32_t kk = float_order(xs);
+    if (kk >= t0) {
+      const int s = atomicAdd(&s_cnt, 1);
+      if (s < kCandMax) sm.row.cand[s] = cand_word(kk, id);
+    }
+    float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
+    d = finite_m ? d : -INFINITY;
+    acc += exp_fixed(d);
+  });
+  __syncthreads();
+  const int ncand = s_cnt;
+  int nsort;
+  if (ncand <= kCandMax) {
+    nsort = ncand;
+  } else {
+    // Exact fallback (rows with very many near-top ties): find the K-th
+    // largest key bit by bit, then keep the keys above it and the lowest ids
+    // among the keys equal to it.
+    uint32_t t = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      int cnt = 0;
+      view.visit_mem(tid, [&](int, float raw) __attribute__((always_inline)) { cnt += key_of(raw) >= c ? 1 : 0; });
+      if (block_sum<BLOCK>(cnt, red_i) >= K) t = c;
+    }
+    int gt = 0;
+    view.visit_mem(tid, [&](int, float raw) __attribute__((always_inline)) { gt += key_of(raw) > t ? 1 : 0; });
+    const int ngt = block_sum<BLOCK>(gt, red_i);
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    view.visit_mem(tid, [&](int id, float raw) __attribute__((always_inline)) {
+      uint32_t kk = key_of(raw);
+      if (kk > t) sm.row.cand[atomicAdd(&s_cnt, 1)] = cand_word(kk, id);
+    });
+    const int need = K - ngt;
+    int base = 0;
+    const int nc = view.num_chunks();
+    for (int c = 0; c < nc && base < need; ++c) {
+      int local = 0;
+      view.visit_chunk(c, tid, [&](int, float raw) __attribute__((always_inline)) { local += key_of(raw) == t ? 1 : 0; });
+      int excl;
+      const int total = block_exclusive_scan<BLOCK>(local, &excl, red_i);
+      int j = 0;
+      view.visit_chunk(c, tid, [&](int id, float raw) __attribute__((always_inline)) {
+        if (key_of(raw) == t) {
+          if (base + excl + j < need) sm.row.cand[atomicAdd(&s_cnt, 1)] = cand_word(t, id);
+          ++j;
+        }
+      });
+      base += total;
+    }
+    __syncthreads();
+    nsort = K;
+  }
+  int P = 2;
+  while (P < nsort) P <<= 1;
+  for (int i = nsort + tid; i < P; i += BLOCK) sm.row.cand[i] = 0;
+  __syncthreads();
+  bitonic_desc<BLOCK>(sm.row.cand, P);
+
+  const uint64_t S = block_sum_u64<BLOCK>((uint64_t)acc, red_u);
+  if (tid == 0) s_lse = (m == -INFINITY) ? INFINITY : lse_from_fixed(S);
+  __syncthreads();
+
+  // ---- the K candidates with their log-probabilities
+  if (tid < K) {
+    const uint64_t c = sm.row.cand[tid];
+    const uint32_t kk = (uint32_t)(c >> 32);
+    const int id = (int)(0xFFFFFFFFu - (uint32_t)c);
+    const float x = order_to_float(kk);
+    float lp;
+    if (m == -INFINITY) {
+      lp = -INFINITY;
+    } else {
+      float d = (GENERAL && mode == 2) ? ((x == m) ? 0.0f : -INFINITY) : (x - m);
+      lp = d - s_lse;
+    }
+    a.topk_tok[(size_t)r * K + tid] = id;
+    a.topk_lp[(size_t)r * K + tid] = lp;
+  }
+  if (tid == 0) a.row_flags[r] = flags;
+
+  // ---- arrival: the last row of request b builds its tree
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int old = atomicAdd(&a.counters[b], 1);
+    s_last = (old == a.L - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (tid == 0) a.counters[b] = 0;
+
+  TreeShared& tr = sm.tree;
+  const int LK = a.L * K;
+  for (int i = tid; i < LK; i += BLOCK) {
+    tr.tok[i] = a.topk_tok[(size_t)b * LK + i];
+    tr.lp[i] = a.topk_lp[(size_t)b * LK + i];
+  }
+  if (tid == 0 && a.status) {
+    int f = 0;
+    for (int i = 0; i < a.L; ++i) f |= a.row_flags[(size_t)b * a.L + i];
+    a.status[b] = f;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const int nn = tree_wave(tr, a.L, K, a.N, a.root_tokens[b]);
+    if (lane == 0) s_nn = nn;
+  }
+  __syncthreads();
+  const int nn = s_nn;
+  const int T = a.N + 1;
+  for (int i = tid; i < T; i += BLOCK) {
+    const size_t o = (size_t)b * T + i;
+    const bool ok = i < nn;
+    a.tokens[o] = ok ? tr.ntok[i] : -1;
+    a.parents[o] = ok ? tr.npar[i] : -1;
+    a.depths[o] = ok ? tr.ndep[i] : -1;
+    a.scores[o] = ok ? tr.nscore[i] : -INFINITY;
+  }
+  if (tid == 0) a.num_nodes[b] = nn;
+  if (a.mask) {
+    const int W = (T + 63) >> 6;
+    for (int idx = tid; idx < T * W; idx += BLOCK) {
+      const int i = idx / W, w = idx - (idx / W) * W;
+      uint64_t bits = 0;
+      if (i < nn) {
+        int j = i;
+        while (j >= 64 * w) {
+          if (j < 64 * (w + 1)) bits |= 1ull << (j - 64 * w);
+          j = tr.npar[j];
+        }
+      }
+      a.mask[((size_t)b * T + i) * W + w] = bits;
+    }
+  }
+}
+
+// Standalone ancestor mask of given trees [BDDT Abstract, §4.1].
+__global__ __launch_bounds__(256) void k_mask(const int32_t* parents, const int32_t* num_nodes,
+                                              int T, uint64_t* mask) {
+  __shared__ int32_t par[kMaxT];
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < T; i += 256) par[i] = parents[(size_t)b * T + i];
+  __syncthreads();
+  const int nn = num_nodes[b];
+  const int W = (T + 63) >> 6;
+  for (int idx = threadIdx.x; idx < T * W; idx += 256) {
+    const int i = idx / W, w = idx - (idx / W) * W;
+    uint64_t bits = 0;
+    if (i < nn) {
+      int j = i;
+      int guard = 0;
+      while (j >= 64 * w && guard++ <= kMaxT) {
+        if (j < 64 * (w + 1)) bits |= 1ull << (j - 64 * w);
+        const int pj = par[j];
+        j = (pj < j) ? pj : -1;  // malformed input (parent >= child) ends the walk
+      }
+    }
+    mask[((size_t)b * T + i) * W + w] = bits;
+  }
+}
+
+template <typename IN_T, int BLOCK, int CH>
+hipError_t launch_t(const BuildArgs& a, hipStream_t st) {
+  dim3 grid(a.batch * a.L), block(BLOCK);
+  if (a.mode == 0) {
+    hipLaunchKernelGGL((k_build<IN_T, BLOCK, CH, false>), grid, block, 0, st, a);
+  } else if constexpr (CH > 16) {
+    // temperature scaling / argmax mode on the longest rows: the streaming
+    // variant (the register-resident one does not fit without spilling)
+    hipLaunchKernelGGL((k_build<IN_T, BLOCK, 0, true>), grid, block, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_build<IN_T, BLOCK, CH, true>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename IN_T>
+hipError_t launch_dt(const BuildArgs& a, hipStream_t st) {
+  constexpr int EPV = Elem<IN_T>::kPerVec;
+  const size_t esize = sizeof(IN_T);
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) &&
+                      ((size_t)a.V * esize) % 16 == 0;
+  if (!vec_ok) return launch_t<IN_T, 256, -1>(a, st);
+  const int nvec = a.V / EPV;
+  if (nvec <= 256) return launch_t<IN_T, 256, 1>(a, st);
+  const int ch = (nvec + 511) / 512;
+  if (ch <= 4) return launch_t<IN_T, 512, 4>(a, st);
+  if (ch <= 8) return launch_t<IN_T, 512, 8>(a, st);
+  if (ch <= 16) return launch_t<IN_T, 512, 16>(a, st);
+  if (ch <= 40) return launch_t<IN_T, 512, 40>(a, st);
+  return launch_t<IN_T, 512, 0>(a, st);
+}
+
+}  // namespace
+
+size_t build_workspace_bytes(int batch, int L, int K) {
+  size_t n = (size_t)batch * L * K;
+  return align_up(n * 4, 256) * 2 + align_up((size_t)batch * L * 4, 256) +
+         align_up((size_t)batch * 4, 256);
+}
+
+void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** topk_lp,
+                 int32_t** row_flags, int32_t** counters) {
+  char* p = static_cast<char*>(ws);
+  size_t n = (size_t)batch * L * K;
+  *topk_tok = reinterpret_cast<int32_t*>(p);
+  p += align_up(n * 4, 256);
+  *topk_lp = reinterpret_cast<float*>(p);
+  p += align_up(n * 4, 256);
+  *row_flags = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)batch * L * 4, 256);
+  *counters = reinterpret_cast<int32_t*>(p);
+}
+
+hipError_t launch_build(const BuildArgs& a, hipStream_t st) {
+  if (a.dtype == 0) return launch_dt<uint16_t>(a, st);
+  return launch_dt<float>(a, st);
+}
+
+hipError_t launch_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,
+                       uint64_t* mask, hipStream_t st) {
+  hipLaunchKernelGGL(k_mask, dim3(batch), dim3(256), 0, st, parents, num_nodes, T, mask);
+  return hipGetLastError();
+}
+
+}  // namespace ddt

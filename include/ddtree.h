@@ -1,0 +1,182 @@
+/*
+ * ddtree.h -- C ABI of the DDTree per-round hot path on AMD Instinct MI355X
+ * (gfx950): draft-tree build, tree-attention verify, greedy acceptance.
+ *
+ * Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees"
+ * (Ringel, Romano), summary page, cited as [BDDT <section>].
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
+ *    row-major and contiguous with the shapes given. The caller owns every
+ *    buffer, including the workspace; the library never allocates device
+ *    memory and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only
+ *    enqueue work and return; results are ready when the stream reaches them.
+ *  - Return value: DDTREE_OK (0) or a negative DDTREE_ERR_* code. Argument
+ *    checks run on the host before anything is enqueued: a call that fails
+ *    them launches nothing and writes nothing. DDTREE_ERR_HIP reports a
+ *    failed launch.
+ *  - Workspaces hold per-call scratch plus small arrival counters. A new
+ *    workspace must be zero-filled once before its first use (e.g.
+ *    torch.zeros); every call leaves the counters at zero again. A workspace
+ *    serves one call at a time: calls that overlap on one workspace race.
+ *  - dtype: DDTREE_BF16 (bfloat16 storage) or DDTREE_F32 (float32 storage).
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DDTREE_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+
+typedef enum { DDTREE_BF16 = 0, DDTREE_F32 = 1 } ddtree_dtype;
+
+enum {
+    DDTREE_OK = 0,
+    DDTREE_ERR_ARG = -1,         /* null pointer, size or range violation   */
+    DDTREE_ERR_UNSUPPORTED = -2, /* dtype / shape outside the limits below  */
+    DDTREE_ERR_WORKSPACE = -3,   /* workspace pointer missing or too small  */
+    DDTREE_ERR_HIP = -4          /* a HIP launch failed                     */
+};
+
+/* Limits. */
+#define DDTREE_MAX_L 64        /* draft block length (positions)           */
+#define DDTREE_MAX_K 32        /* candidates per position                  */
+#define DDTREE_MAX_N 1024      /* node budget                              */
+#define DDTREE_MAX_V (1 << 19) /* vocabulary                               */
+
+/* Bits of status_flags[b] written by ddtree_build. */
+#define DDTREE_STATUS_NONFINITE 1   /* a NaN or +inf logit was ranked as -inf */
+#define DDTREE_STATUS_ALL_NEG_INF 2 /* a position had no finite logit         */
+
+/* Library version (DDTREE_VERSION of the build). Host only. */
+int ddtree_version(void);
+
+/* Static text for a return code. Host only. */
+const char *ddtree_strerror(int status);
+
+/*
+ * ddtree_build -- one drafter block's per-position distributions to a
+ * budget-bounded draft tree.                 [BDDT §3, §4.1, §4.2, §4.3, App. A]
+ *
+ * Per request b and position i (0-based, depth i+1), the row
+ * logits[b, i, 0..V) is turned into log-probabilities of
+ * softmax(logits / draft_temp) with a fixed, bit-reproducible arithmetic
+ * (fp32 values, exact uint64 fixed-point sum, fp64 logarithm), and its K best
+ * tokens (logit desc, token id asc). draft_temp = 0 is the argmax limit
+ * (tied maxima share the mass, the others get -inf). NaN and +inf are ranked
+ * as -inf and flagged.
+ *
+ * The tree is rooted at root_tokens[b] (the bonus token, node 0, depth 0,
+ * score 0). N best-first pops follow: the candidate with the highest
+ * cumulative log-probability (ties: shallower depth, then lower parent node
+ * index, then lower rank) becomes the next node; it pushes its next sibling
+ * and its best child. Scores accumulate in fp32 from the root. Nodes are
+ * numbered in pop order, so parents[i] < i.
+ *
+ *   logits        [batch, L, V] dt                   in
+ *   root_tokens   [batch] int32                      in
+ *   tokens, parents, depths  [batch, N+1] int32      out (padding rows -1)
+ *   scores        [batch, N+1] float32               out (padding rows -inf)
+ *   num_nodes     [batch] int32                      out (root included)
+ *   mask          [batch, N+1, W] uint64 or NULL     out, W = ceil((N+1)/64):
+ *                 bit j of row i (word j/64, bit j%64) is set iff node j is
+ *                 node i or one of its ancestors; padding rows are zero
+ *   topk_tokens   [batch, L, K] int32 or NULL        out
+ *   topk_logprobs [batch, L, K] float32 or NULL      out
+ *   status_flags  [batch] int32 or NULL              out (DDTREE_STATUS_*)
+ *   workspace     >= ddtree_build_workspace_size(...) bytes, zeroed once
+ *
+ * Limits: 1 <= batch; 1 <= L <= 64; 1 <= K <= min(32, V); 1 <= N <= 1024;
+ * V <= 2^19; draft_temp >= 0 and finite.
+ */
+size_t ddtree_build_workspace_size(int batch, int L, int V, int K, int N);
+int ddtree_build(const void *logits, ddtree_dtype dt, const int32_t *root_tokens, int batch,
+                 int L, int V, int K, int N, float draft_temp, int32_t *tokens,
+                 int32_t *parents, int32_t *depths, float *scores, int32_t *num_nodes,
+                 uint64_t *mask, int32_t *topk_tokens, float *topk_logprobs,
+                 int32_t *status_flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ddtree_mask -- ancestor-only attention bitmask of given trees.
+ *                                                        [BDDT Abstract, §4.1]
+ *   parents   [batch, T] int32 (parents[b, i] < i; -1 at the root)   in
+ *   num_nodes [batch] int32 (1 <= num_nodes[b] <= T)                  in
+ *   mask      [batch, T, W] uint64, W = ceil(T/64)                    out
+ * Same bit layout as in ddtree_build. Limits: 1 <= T <= 1025.
+ */
+int ddtree_mask(const int32_t *parents, const int32_t *num_nodes, int batch, int T,
+                uint64_t *mask, void *stream);
+
+/*
+ * ddtree_verify_attn -- one attention layer of the tree verification pass.
+ *                                               [BDDT Abstract, §4.1, App. B]
+ * Query row (b, i, h) -- node i of request b, query head h -- attends to all
+ * P_b prefix keys of request b and to the tree keys j whose mask bit (i, j)
+ * is set, with softmax(scale * q.k) weights over V. Query head h reads key /
+ * value head h / (Hq / Hkv) (grouped-query attention).
+ *
+ *   q, out        [batch, T, Hq, D] dt                  in / out
+ *   k, v          [rows, Hkv, D] dt                     in; request b owns rows
+ *                 kv_offsets[b] .. kv_offsets[b] + P_b + T: first its P_b
+ *                 prefix rows, then one row per tree node in node order
+ *                 (the caller writes the tree rows before the call)
+ *   kv_offsets    [batch] int64                         in
+ *   prefix_lens   [batch] int32 (P_b >= 0)              in
+ *   num_nodes     [batch] int32                         in; rows i >= num_nodes[b]
+ *                 are written as zeros
+ *   mask          [batch, T, ceil(T/64)] uint64         in (layout of ddtree_build)
+ *   max_prefix_len  an upper bound on every P_b (sizes the work split)
+ *   total_rows    number of rows of k and v (bounds checking)
+ *   softmax_scale <= 0 selects 1/sqrt(D)
+ *   workspace     >= ddtree_verify_workspace_size(...) bytes, zeroed once
+ *
+ * bf16: fp32 accumulation on MFMA, bf16 output. f32: fp32 throughout.
+ * Limits: Hq % Hkv == 0; T <= 1025; D in {32, 64, 128} (bf16: D = 128).
+ */
+size_t ddtree_verify_workspace_size(ddtree_dtype dt, int batch, int T, int Hq, int Hkv, int D,
+                                    int max_prefix_len);
+int ddtree_verify_attn(const void *q, const void *k, const void *v, ddtree_dtype dt,
+                       const int64_t *kv_offsets, const int32_t *prefix_lens,
+                       const int32_t *num_nodes, const uint64_t *mask, int batch, int T, int Hq,
+                       int Hkv, int D, int max_prefix_len, int64_t total_rows,
+                       float softmax_scale, void *out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * ddtree_accept -- greedy acceptance walk.                        [BDDT §4.1]
+ * The target's token after node i is argmax_v target_logits[b, i, v] (first
+ * maximal index; NaN counts as -inf), or target_ids[b, i] when
+ * target_logits is NULL. From the root, the walk follows the child whose
+ * token equals the target's token; the matched path is accepted and the first
+ * unmatched target token is the bonus (the next round's root).
+ *
+ *   target_logits   [batch, T, V] dt, or NULL             in
+ *   target_ids      [batch, T] int32 (used when target_logits is NULL)  in
+ *   tokens, parents [batch, T] int32, num_nodes [batch]   in (ddtree_build output)
+ *   accepted        [batch, L] int32                      out: accepted tokens, -1 padded
+ *   accepted_nodes  [batch, L] int32 or NULL              out: their node indices
+ *   accept_len      [batch] int32                         out
+ *   bonus           [batch] int32                         out
+ *   target_argmax   [batch, T] int32 or NULL              out: the target token
+ *                   per node (-1 for rows >= num_nodes[b])
+ *   workspace       >= ddtree_accept_workspace_size(...) bytes, zeroed once
+ * Limits: T <= 1025, 1 <= L <= 64, V <= 2^31 - 1 (logits path: V >= 1).
+ */
+size_t ddtree_accept_workspace_size(int batch, int T);
+int ddtree_accept(const void *target_logits, ddtree_dtype dt, const int32_t *target_ids,
+                  const int32_t *tokens, const int32_t *parents, const int32_t *num_nodes,
+                  int batch, int T, int V, int L, int32_t *accepted, int32_t *accepted_nodes,
+                  int32_t *accept_len, int32_t *bonus, int32_t *target_argmax, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDTREE_H */

@@ -8,3 +8,16 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an AMD Instinct GPU (gfx950) through the C ABI")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu_required(request):
+    """GPU tests fail loudly (never skip) when no HIP device is visible."""
+    if request.node.get_closest_marker("gpu") is not None:
+        import torch
+        if not torch.cuda.is_available():
+            pytest.fail("test marked gpu but no HIP device is visible")
+    yield

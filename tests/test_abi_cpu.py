@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/ddtree.h, and rejects bad arguments on the host before
+anything would be enqueued (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_tree_build_amd as dtb
+from draft_tree_build_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddtree.h")
+
+OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP = 0, -1, -2, -3, -4
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddtree_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 9, names
+    L = ctypes.CDLL(api.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_strerror_and_sizes():
+    assert dtb.version() == 10000
+    for code in (OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP):
+        assert dtb.strerror(code) and dtb.strerror(code) != "unknown status"
+    assert dtb.strerror(-99) == "unknown status"
+    assert dtb.ddtree_build_workspace_size(32, 16, 151936, 8, 128) >= 32 * 16 * 8 * 8
+    assert dtb.ddtree_build_workspace_size(0, 16, 100, 8, 8) == 0
+    assert dtb.ddtree_accept_workspace_size(4, 513) >= 4 * 513 * 4
+    # split-KV partials only when a small batch meets a long prefix
+    small = dtb.ddtree_verify_workspace_size(0, 1, 65, 32, 8, 128, 2048)
+    big = dtb.ddtree_verify_workspace_size(0, 4, 513, 64, 8, 128, 65536)
+    assert small > 1 << 20 and big == 256
+    assert dtb.ddtree_verify_workspace_size(0, 1, 65, 30, 8, 128, 2048) == 0  # Hq % Hkv
+
+
+# Host validation. Pointers are fake non-null addresses: every case below has
+# exactly one invalid field and must be rejected before any HIP call.
+P = ctypes.c_void_p(0x1000)
+N0 = None
+
+
+def _no_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-validation cases use fake pointers; run them where no GPU is visible")
+
+
+def _build(**kw):
+    a = dict(logits=P, dt=0, root=P, batch=2, L=4, V=64, K=4, N=8, temp=1.0, tokens=P, parents=P,
+             depths=P, scores=P, nn=P, mask=N0, tk=N0, tl=N0, st=N0, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return api.lib().ddtree_build(a["logits"], a["dt"], a["root"], a["batch"], a["L"], a["V"],
+                                  a["K"], a["N"], a["temp"], a["tokens"], a["parents"], a["depths"],
+                                  a["scores"], a["nn"], a["mask"], a["tk"], a["tl"], a["st"],
+                                  a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=N0), ERR_ARG), (dict(tokens=N0), ERR_ARG), (dict(nn=N0), ERR_ARG),
+    (dict(batch=0), ERR_ARG), (dict(L=0), ERR_ARG), (dict(K=0), ERR_ARG), (dict(N=0), ERR_ARG),
+    (dict(K=65, V=64), ERR_ARG), (dict(temp=-1.0), ERR_ARG), (dict(temp=float("inf")), ERR_ARG),
+    (dict(temp=float("nan")), ERR_ARG), (dict(dt=7), ERR_UNSUP), (dict(K=33, V=100), ERR_UNSUP),
+    (dict(N=1025), ERR_UNSUP), (dict(L=65), ERR_UNSUP), (dict(V=(1 << 19) + 1), ERR_UNSUP),
+    (dict(ws=N0), ERR_WS), (dict(wsb=16), ERR_WS),
+])
+def test_build_rejects(kw, code):
+    _no_gpu()
+    assert _build(**kw) == code
+
+
+def _verify(**kw):
+    a = dict(q=P, k=P, v=P, dt=0, offs=P, pl=P, nn=P, mask=P, batch=1, T=9, Hq=4, Hkv=2, D=128,
+             maxp=16, rows=100, scale=0.0, out=P, ws=P, wsb=1 << 24)
+    a.update(kw)
+    return api.lib().ddtree_verify_attn(a["q"], a["k"], a["v"], a["dt"], a["offs"], a["pl"],
+                                        a["nn"], a["mask"], a["batch"], a["T"], a["Hq"], a["Hkv"],
+                                        a["D"], a["maxp"], a["rows"], a["scale"], a["out"],
+                                        a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=N0), ERR_ARG), (dict(mask=N0), ERR_ARG), (dict(out=N0), ERR_ARG),
+    (dict(Hq=5), ERR_ARG), (dict(T=0), ERR_ARG), (dict(maxp=-1), ERR_ARG), (dict(rows=0), ERR_ARG),
+    (dict(scale=float("nan")), ERR_ARG), (dict(dt=3), ERR_UNSUP), (dict(D=96), ERR_UNSUP),
+    (dict(D=64), ERR_UNSUP), (dict(T=1026), ERR_UNSUP), (dict(ws=N0), ERR_WS),
+    (dict(wsb=0), ERR_WS),
+])
+def test_verify_rejects(kw, code):
+    _no_gpu()
+    assert _verify(**kw) == code
+
+
+def _accept(**kw):
+    a = dict(tl=P, dt=0, ids=N0, tok=P, par=P, nn=P, batch=1, T=9, V=64, L=4, acc=P, accn=N0,
+             alen=P, bonus=P, targ=N0, ws=P, wsb=1 << 16)
+    a.update(kw)
+    return api.lib().ddtree_accept(a["tl"], a["dt"], a["ids"], a["tok"], a["par"], a["nn"],
+                                   a["batch"], a["T"], a["V"], a["L"], a["acc"], a["accn"],
+                                   a["alen"], a["bonus"], a["targ"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tl=N0), ERR_ARG), (dict(tok=N0), ERR_ARG), (dict(bonus=N0), ERR_ARG),
+    (dict(L=0), ERR_ARG), (dict(V=0), ERR_ARG), (dict(batch=0), ERR_ARG), (dict(dt=9), ERR_UNSUP),
+    (dict(L=65), ERR_UNSUP), (dict(T=2000), ERR_UNSUP), (dict(wsb=4), ERR_WS),
+])
+def test_accept_rejects(kw, code):
+    _no_gpu()
+    assert _accept(**kw) == code
+
+
+def test_mask_rejects():
+    _no_gpu()
+    L = api.lib()
+    assert L.ddtree_mask(None, P, 1, 9, P, None) == ERR_ARG
+    assert L.ddtree_mask(P, P, 0, 9, P, None) == ERR_ARG
+    assert L.ddtree_mask(P, P, 1, 2000, P, None) == ERR_UNSUP

@@ -1,0 +1,131 @@
+"""GPU parity of ddtree_build / ddtree_mask against the oracle: bit-exact.
+
+Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees",
+§3, §4.1-4.3, App. A. Covers every kernel variant (register-resident rows of
+several lengths, streaming rows, unaligned rows), temperature 1 / scaled / 0,
+the exact fallback of the top-K selection, non-finite and all -inf rows,
+budget and block limits, and the full-size workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_tree_build_amd import api, synth
+from gpu_util import DEV, assert_same_build, gpu_build, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _logits(B, L, V, seed, sigma=3.0, dtype=torch.bfloat16, boost=8.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(B, L, V, generator=g) * sigma
+    if boost:
+        idx = torch.randint(0, V, (B, L), generator=g)
+        x.scatter_add_(2, idx[..., None], torch.full((B, L, 1), boost))
+    return x.to(dtype)
+
+
+CASES = [
+    # (B, L, V, K, N, dtype) -- V picks the kernel variant
+    (1, 4, 64, 4, 8, torch.float32),          # 256 threads, one vector per thread
+    (2, 5, 1000, 8, 30, torch.bfloat16),      # 256 threads
+    (2, 3, 1001, 6, 20, torch.bfloat16),      # unaligned rows: scalar path
+    (1, 6, 1001, 5, 25, torch.float32),       # unaligned f32
+    (3, 8, 5000, 8, 64, torch.bfloat16),      # 512 threads, 4 vectors per thread
+    (1, 16, 32000, 8, 64, torch.bfloat16),    # 8 vectors per thread
+    (2, 7, 60000, 16, 100, torch.bfloat16),   # 16 vectors per thread
+    (1, 5, 60000, 16, 100, torch.float32),
+    (2, 4, 151936, 16, 50, torch.bfloat16),   # 40 vectors per thread
+    (1, 3, 151936, 8, 20, torch.float32),     # streaming
+    (1, 3, 400000, 32, 40, torch.bfloat16),   # streaming
+]
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.7, 0.0])
+@pytest.mark.parametrize("B,L,V,K,N,dtype", CASES)
+def test_build_matches_oracle(B, L, V, K, N, dtype, tau):
+    x = _logits(B, L, V, seed=V + K + N, dtype=dtype)
+    roots = torch.arange(B, dtype=torch.int32) * 7 % V
+    note("build B=%d L=%d V=%d K=%d N=%d %s tau=%g" % (B, L, V, K, N, dtype, tau))
+    g, _ = gpu_build(x, roots, K, N, tau)
+    o = oracle.build_tree(x, roots, K, N, tau)
+    assert_same_build(g, o)
+
+
+def test_build_adversarial_rows():
+    B, L, V, K, N = 2, 6, 5000, 16, 120
+    x = _logits(B, L, V, seed=5, dtype=torch.float32)
+    x[0, 0] = 1.5                                  # all equal: exact fallback (ties > buffer)
+    x[0, 1] = torch.randint(-3, 3, (V,)).float()   # heavy ties at the top
+    x[0, 2, 17] = float("nan")
+    x[0, 2, 99] = float("inf")
+    x[1, 0] = float("-inf")                        # no finite logit
+    x[1, 1, :4000] = float("-inf")
+    x[1, 2] = torch.where(torch.arange(V) % 3 == 0, torch.tensor(2.0), torch.tensor(float("-inf")))
+    for tau in (1.0, 0.5, 0.0):
+        for dtype in (torch.float32, torch.bfloat16):
+            xd = x.to(dtype)
+            note("build adversarial dtype=%s tau=%g" % (dtype, tau))
+            g, _ = gpu_build(xd, [3, 4], K, N, tau)
+            o = oracle.build_tree(xd, [3, 4], K, N, tau)
+            assert_same_build(g, o)
+            assert g["status"][0] & 1 and g["status"][1] & 2
+
+
+@pytest.mark.parametrize("L,K,N", [(1, 1, 1), (1, 32, 1024), (64, 1, 64), (64, 2, 1024),
+                                   (2, 2, 10), (16, 32, 1024), (33, 3, 700)])
+def test_build_limits(L, K, N):
+    x = _logits(2, L, 3000, seed=L * K + N, sigma=2.0)
+    note("build limits L=%d K=%d N=%d" % (L, K, N))
+    g, _ = gpu_build(x, [1, 2], K, N, 1.0)
+    o = oracle.build_tree(x, [1, 2], K, N, 1.0)
+    assert_same_build(g, o)
+
+
+def test_build_repeatable_on_one_workspace():
+    """Two calls on one workspace: the arrival counters are left at zero."""
+    x = _logits(4, 8, 2000, seed=3)
+    ws = api.new_workspace(api.ddtree_build_workspace_size(4, 8, 2000, 8, 40), DEV)
+    note("build twice on one workspace")
+    g1, _ = gpu_build(x, [0, 1, 2, 3], 8, 40, 1.0, ws=ws)
+    g2, _ = gpu_build(x, [0, 1, 2, 3], 8, 40, 1.0, ws=ws)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k], g2[k])
+    n = 4 * 8 * 8
+    al = lambda x: (x + 255) // 256 * 256
+    off = al(4 * n) * 2 + al(4 * 4 * 8)
+    assert not ws[off:off + 16].cpu().any()  # the four arrival counters are back at zero
+    o = oracle.build_tree(x, [0, 1, 2, 3], 8, 40, 1.0)
+    assert_same_build(g2, o)
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_build_full_size_workloads(name):
+    w = synth.WORKLOADS[name]
+    x, _ = synth.drafter_logits(w)
+    roots = synth.root_tokens(w)
+    for tau in w.taus:
+        note("build workload %s tau=%g" % (name, tau))
+        g, _ = gpu_build(x, roots, w.K, w.N, tau)
+        o = oracle.build_tree(x, roots, w.K, w.N, tau)
+        assert_same_build(g, o)
+
+
+def test_mask_matches_oracle():
+    rng = np.random.default_rng(0)
+    for T in (1, 9, 64, 65, 129, 513, 1025):
+        B = 3
+        par = np.full((B, T), -1, np.int32)
+        nn = np.zeros(B, np.int32)
+        for b in range(B):
+            n = T if b == 0 else int(rng.integers(1, T + 1))
+            nn[b] = n
+            for i in range(1, n):
+                par[b, i] = int(rng.integers(0, i)) if b != 2 else i - 1
+        mask = torch.empty(B, T, (T + 63) // 64, dtype=torch.int64, device=DEV)
+        note("mask T=%d" % T)
+        api.ddtree_mask(torch.from_numpy(par).to(DEV), torch.from_numpy(nn).to(DEV), mask)
+        got = mask.cpu().numpy().view(np.uint64)
+        for b in range(B):
+            np.testing.assert_array_equal(got[b], oracle.mask(par[b], nn[b], T))
