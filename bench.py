@@ -38,7 +38,8 @@ KERNEL_SOURCES = {
     "verify": "draft_tree_build_amd/csrc/k_attn.hip",
     "accept": "draft_tree_build_amd/csrc/k_accept.hip",
 }
-KERNEL_NAMES = {"build": "k_build", "verify": "k_attn_mfma", "accept": "k_argmax_walk"}
+KERNEL_NAMES = {"build": "k_rows+k_tree", "verify": "k_attn_mfma(+k_attn_combine)",
+                "accept": "k_argmax+k_walk"}
 
 
 def log(msg):
@@ -114,6 +115,8 @@ def main():
                     help="rotate input copies until their total exceeds this (0: one copy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graphs", dest="graphs", action="store_false",
+                    help="launch the ABI calls eagerly instead of replaying captured HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -154,26 +157,53 @@ def main():
     rnd = api.Round(w.batch, w.L, w.V, w.K, w.N, dev, w.Hq, w.Hkv, w.D, int(w.prefix[1]),
                     dtype=w.torch_dtype)
 
-    def step(i, ev=None):
-        x, q, k, v, tl = copies[i % R]
-        if ev is not None:
-            ev[0].record()
-        rnd.build(x, roots, tau)
-        if ev is not None:
-            ev[1].record()
-        rnd.verify(q, k, v, offs, P)
-        if ev is not None:
-            ev[2].record()
-        rnd.accept(tl)
-        if ev is not None:
-            ev[3].record()
+    stages = (
+        lambda c: rnd.build(c[0], roots, tau),
+        lambda c: rnd.verify(c[1], c[2], c[3], offs, P),
+        lambda c: rnd.accept(c[4]),
+    )
 
-    log("warmup %d steps" % args.warmup)
+    log("warmup %d steps (eager)" % args.warmup)
     for i in range(args.warmup):
-        step(i)
+        for f in stages:
+            f(copies[i % R])
     torch.cuda.synchronize()
     num_nodes = rnd.num_nodes.cpu()
     nodes_per_step = int((num_nodes - 1).sum())
+
+    # One HIP graph per (input copy, stage): the three ABI calls of a round
+    # replay without host launch overhead; events between the graph launches
+    # time each stage inside the timed region.
+    graphs = None
+    if args.graphs:
+        log("capturing %d x 3 graphs" % R)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(side):
+            for c in range(R):
+                row = []
+                for f in stages:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=side):
+                        f(copies[c])
+                    row.append(g)
+                graphs.append(row)
+        torch.cuda.current_stream().wait_stream(side)
+        for i in range(min(R, args.warmup)):
+            for g in graphs[i]:
+                g.replay()
+        torch.cuda.synchronize()
+
+    def step(i, ev):
+        c = i % R
+        ev[0].record()
+        for k in range(3):
+            if graphs is not None:
+                graphs[c][k].replay()
+            else:
+                stages[k](copies[c])
+            ev[k + 1].record()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log("timing %d steps" % args.steps)
@@ -231,7 +261,7 @@ def main():
                 "Q/K/V ~N(0,1))",
         "config": {"workload": w.name, "batch": w.batch, "L": w.L, "V": w.V, "K": w.K, "N": w.N,
                    "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                   "draft_temp": tau, "input_copies": R},
+                   "draft_temp": tau, "input_copies": R, "hip_graphs": bool(args.graphs)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,

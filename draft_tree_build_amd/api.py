@@ -113,7 +113,7 @@ def ddtree_accept_workspace_size(batch: int, T: int) -> int:
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled byte buffer (the ABI requires zero on first use)."""
+    """A device byte buffer for a workspace argument (zero-filled for tidiness)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 

@@ -79,13 +79,12 @@ int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens
   a.num_nodes = num_nodes;
   a.mask = mask;
   a.status = status_flags;
-  int32_t *ws_tok, *ws_flags, *ws_cnt;
+  int32_t *ws_tok, *ws_flags;
   float* ws_lp;
-  build_carve(workspace, batch, L, K, &ws_tok, &ws_lp, &ws_flags, &ws_cnt);
+  build_carve(workspace, batch, L, K, &ws_tok, &ws_lp, &ws_flags);
   a.topk_tok = topk_tokens ? topk_tokens : ws_tok;
   a.topk_lp = topk_logprobs ? topk_logprobs : ws_lp;
   a.row_flags = ws_flags;
-  a.counters = ws_cnt;
   return hip_status(launch_build(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -180,10 +179,9 @@ int ddtree_accept(const void* target_logits, ddtree_dtype dt, const int32_t* tar
   a.accepted_nodes = accepted_nodes;
   a.accept_len = accept_len;
   a.bonus = bonus;
-  int32_t *ws_tgt, *ws_cnt;
-  accept_carve(workspace, batch, T, &ws_tgt, &ws_cnt);
+  int32_t* ws_tgt;
+  accept_carve(workspace, batch, T, &ws_tgt);
   a.target_argmax = target_argmax ? target_argmax : ws_tgt;
-  a.counters = ws_cnt;
   return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -25,11 +25,10 @@ struct BuildArgs {
   float* topk_lp;
   int32_t* status;          // may be null
   int32_t* row_flags;       // workspace [batch, L]
-  int32_t* counters;        // workspace [batch], zero between calls
 };
 size_t build_workspace_bytes(int batch, int L, int K);
 void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** topk_lp,
-                 int32_t** row_flags, int32_t** counters);
+                 int32_t** row_flags);
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
 hipError_t launch_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,
@@ -69,10 +68,9 @@ struct AcceptArgs {
   int32_t* accept_len;
   int32_t* bonus;
   int32_t* target_argmax;     // caller output or workspace
-  int32_t* counters;          // workspace [batch]
 };
 size_t accept_workspace_bytes(int batch, int T);
-void accept_carve(void* ws, int batch, int T, int32_t** tgt, int32_t** counters);
+void accept_carve(void* ws, int batch, int T, int32_t** tgt);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

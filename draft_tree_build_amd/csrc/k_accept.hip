@@ -5,11 +5,10 @@
 // decoding rule; the matched path is accepted and the first unmatched target
 // token becomes the next bonus token. At temperature 0 the rule is argmax.
 //
-// Grid: one workgroup per (request, node) row of the target logits, streamed
-// once with 16-byte loads; rows past num_nodes are skipped. The last
-// workgroup of a request to finish (arrival counter) runs the walk with one
-// wavefront: at most L steps, each a ballot over the node's candidate
-// children.
+// k_argmax: one workgroup per (request, node) row of the target logits,
+// streamed once with 16-byte loads (8 in flight per thread); rows past
+// num_nodes are skipped. k_walk: one wavefront per request, at most L steps,
+// each a ballot over the current node's children.
 #include "ddtree_device.h"
 #include "ddtree_internal.h"
 
@@ -70,11 +69,9 @@ __device__ void walk_wave(const AcceptArgs& a, int b, const int32_t* tgt_row, in
 }
 
 template <typename IN_T, int BLOCK, bool VEC>
-__global__ __launch_bounds__(BLOCK) void k_argmax_walk(AcceptArgs a) {
+__global__ __launch_bounds__(BLOCK) void k_argmax(AcceptArgs a) {
   __shared__ float s_v[BLOCK / 64];
   __shared__ int s_i[BLOCK / 64];
-  __shared__ int s_last;
-  __shared__ int32_t s_tok[kMaxT], s_par[kMaxT], s_tgt[kMaxT];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int T = a.T;
   const int rowi = blockIdx.x;
@@ -88,25 +85,33 @@ __global__ __launch_bounds__(BLOCK) void k_argmax_walk(AcceptArgs a) {
     int bi = 0x7FFFFFFF;
     if constexpr (VEC) {
       constexpr int EPV = 16 / sizeof(IN_T);
+      constexpr int U = 8;  // 16-byte loads in flight per thread
       const int nvec = a.V / EPV;
       const uint4* p = reinterpret_cast<const uint4*>(row);
       if (tid < nvec) bi = tid * EPV;
-      for (int vi = tid; vi < nvec; vi += BLOCK) {
-        const uint4 u = p[vi];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-        if constexpr (sizeof(IN_T) == 2) {
+      for (int base = tid; base < nvec; base += BLOCK * U) {
+        uint4 u[U];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x0 = __uint_as_float(w[j] << 16);
-            const float x1 = __uint_as_float(w[j] & 0xFFFF0000u);
-            if (x0 > best) { best = x0; bi = vi * EPV + 2 * j; }
-            if (x1 > best) { best = x1; bi = vi * EPV + 2 * j + 1; }
-          }
-        } else {
+        for (int j = 0; j < U; ++j) u[j] = p[min(base + j * BLOCK, nvec - 1)];  // clamped: always in bounds
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = __uint_as_float(w[j]);
-            if (x > best) { best = x; bi = vi * EPV + j; }
+        for (int j = 0; j < U; ++j) {
+          const int vi = base + j * BLOCK;
+          if (vi >= nvec) break;
+          const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+          if constexpr (sizeof(IN_T) == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float x0 = __uint_as_float(w[q] << 16);
+              const float x1 = __uint_as_float(w[q] & 0xFFFF0000u);
+              if (x0 > best) { best = x0; bi = vi * EPV + 2 * q; }
+              if (x1 > best) { best = x1; bi = vi * EPV + 2 * q + 1; }
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float x = __uint_as_float(w[q]);
+              if (x > best) { best = x; bi = vi * EPV + q; }
+            }
           }
         }
       }
@@ -138,17 +143,6 @@ __global__ __launch_bounds__(BLOCK) void k_argmax_walk(AcceptArgs a) {
     tgt[rowi] = -1;
   }
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = atomicAdd(&a.counters[b], 1);
-    s_last = (old == T - 1) ? 1 : 0;
-    if (s_last) a.counters[b] = 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (wid == 0) walk_wave(a, b, tgt + (size_t)b * T, s_tok, s_par, s_tgt);
 }
 
 // Walk only, from given target ids.
@@ -163,29 +157,36 @@ __global__ __launch_bounds__(64) void k_walk_ids(AcceptArgs a) {
   walk_wave(a, b, a.target_ids + (size_t)b * a.T, s_tok, s_par, s_tgt);
 }
 
+// The walk of one request from its per-node target tokens.
+__global__ __launch_bounds__(64) void k_walk(AcceptArgs a) {
+  __shared__ int32_t s_tok[kMaxT], s_par[kMaxT], s_tgt[kMaxT];
+  const int b = blockIdx.x;
+  walk_wave(a, b, a.target_argmax + (size_t)b * a.T, s_tok, s_par, s_tgt);
+}
+
 template <typename IN_T>
 hipError_t launch_logits(const AcceptArgs& a, hipStream_t st) {
   const bool vec = (reinterpret_cast<uintptr_t>(a.target_logits) % 16 == 0) &&
                    ((size_t)a.V * sizeof(IN_T)) % 16 == 0;
   dim3 grid(a.batch * a.T);
   if (vec)
-    hipLaunchKernelGGL((k_argmax_walk<IN_T, 256, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_argmax<IN_T, 256, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_argmax_walk<IN_T, 256, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_argmax<IN_T, 256, false>), grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_walk, dim3(a.batch), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t accept_workspace_bytes(int batch, int T) {
-  return align_up((size_t)batch * T * 4, 256) + align_up((size_t)batch * 4, 256);
-}
+size_t accept_workspace_bytes(int batch, int T) { return align_up((size_t)batch * T * 4, 256); }
 
-void accept_carve(void* ws, int batch, int T, int32_t** tgt, int32_t** counters) {
-  char* p = static_cast<char*>(ws);
-  *tgt = reinterpret_cast<int32_t*>(p);
-  p += align_up((size_t)batch * T * 4, 256);
-  *counters = reinterpret_cast<int32_t*>(p);
+void accept_carve(void* ws, int batch, int T, int32_t** tgt) {
+  (void)batch;
+  (void)T;
+  *tgt = reinterpret_cast<int32_t*>(ws);
 }
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {

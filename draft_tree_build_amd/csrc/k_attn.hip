@@ -16,7 +16,7 @@
 // (lane = query row), online softmax in fp32 (exp2 domain), O^T += V^T P^T
 // with P split into two bf16 parts (hi + lo) so the weights stay ~fp32 exact.
 // The key tile list is prefix tiles then tree tiles (mask applied); long
-// lists are split across workgroups and merged by the last split to arrive
+// lists are split across workgroups and merged by a second kernel
 // (log-sum-exp weights).
 //
 // f32 (k_attn_simple): one thread per query row, fp32 throughout.
@@ -35,13 +35,18 @@ constexpr int kTileRows = kRowsPerWave * kWavesA;  // 128
 constexpr int kKeys = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// K tile: [64 keys][16 chunks of 8 dims]; chunk index XOR-swizzled by key so
-// that the 8 lanes of a 128-bit LDS access hit distinct banks.
-__device__ __forceinline__ int k_lds_off(int key, int chunk) {
-  int sw = (key & 3) | ((key >> 1) & 4);
-  return key * (kD * 2) + ((chunk ^ sw) << 4);
-}
-// V^T tile: [128 dims][8 chunks of 8 keys]; chunk swizzled by dim.
+// K tile: 64 rows of 256 bytes (128 dims), row r at byte r*272 + (r/8)*64.
+// The padding puts the 8 lanes of a 128-bit fragment read -- keys
+// {0..3, 8..11} + c or {4..7, 12..15} + c -- on 8 distinct 16-byte bank
+// groups, and every fragment offset of a lane is a compile-time immediate.
+constexpr int kKRow = kD * 2 + 16;
+constexpr int kKBytes = (kKeys - 1) * kKRow + (kKeys / 8 - 1) * 64 + kD * 2;
+__device__ __forceinline__ int k_row_off(int key) { return key * kKRow + (key >> 3) * 64; }
+// V^T tile: [128 dims][8 chunks of 8 keys] = 128 bytes per dim, chunk index
+// XOR-swizzled by sw(dim) = (dim ^ (dim >> 3)) & 7. Fragment reads (32
+// consecutive dims) and transposed writes (dims 8 apart) both spread over
+// the banks; for dim = 32 db + n, sw = ((n ^ (n >> 3)) & 7) ^ 4 (db & 1).
+constexpr int kVBytes = kKeys * kD * 2;
 __device__ __forceinline__ int v_lds_off(int dim, int chunk) {
   int sw = (dim ^ (dim >> 3)) & 7;
   return dim * (kKeys * 2) + ((chunk ^ sw) << 4);
@@ -50,19 +55,30 @@ __device__ __forceinline__ int v_lds_off(int dim, int chunk) {
 struct AttnSplit {
   int nsplit;
   int row_tiles;
+  int total;    // work items: batch * Hkv * nsplit * row_tiles
+  int per_xcd;  // work items per XCD slice of the grid
 };
 
-__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int nsplit, int row_tiles,
-                                                      float* part_o, float* part_ml,
-                                                      int32_t* counters) {
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[kKeys * kD * 2];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[kKeys * kD * 2];
-  __shared__ int s_last;
+constexpr int kXcds = 8;
 
+// One workgroup = 128 query rows of one (request, kv-head) over one range of
+// key tiles. Grid: 1-D, XCD-aware -- consecutive workgroup ids go to
+// different XCDs, so work item w runs as workgroup (w % per_xcd) * 8 + w /
+// per_xcd, which keeps all row tiles of one (request, kv-head, split) on one
+// XCD and its K/V tiles in that XCD's L2. Key tiles are double-buffered in
+// LDS: tile t+1 is fetched into registers while tile t is computed.
+__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, float* part_o,
+                                                      float* part_ml) {
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kKBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][kVBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int xt = blockIdx.x;
-  const int b = blockIdx.y / a.Hkv, hk = blockIdx.y - (blockIdx.y / a.Hkv) * a.Hkv;
-  const int z = blockIdx.z;
+  const int wi = (int)(blockIdx.x % kXcds) * pl.per_xcd + (int)(blockIdx.x / kXcds);
+  if (wi >= pl.total) return;
+  const int nsplit = pl.nsplit, row_tiles = pl.row_tiles;
+  const int xt = wi % row_tiles;
+  const int z = (wi / row_tiles) % nsplit;
+  const int bhi = wi / (row_tiles * nsplit);
+  const int b = bhi / a.Hkv, hk = bhi - (bhi / a.Hkv) * a.Hkv;
   const int g = a.Hq / a.Hkv;
   const int T = a.T;
   const int R = T * g;
@@ -127,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int nsplit, in
   const int dc = lane & 15, kq = lane >> 4;
   const int k0 = 16 * w + 2 * kq;
   uint4 sk[4], sv[4];
-  auto tile_rows = [&](int t, int* base, int* nvalid) {
+  auto tile_rows = [&](int t, int* base, int* nvalid) __attribute__((always_inline)) {
     if (t < np) {
       *base = t * kKeys;
       *nvalid = min(kKeys, P - t * kKeys);
@@ -137,37 +153,37 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int nsplit, in
       *nvalid = min(kKeys, nn - tt * kKeys);
     }
   };
-  auto load_tile = [&](int t) {
+  // per-lane element offsets inside a tile (32-bit); the tile base is uniform
+  const uint32_t row_elems = (uint32_t)a.Hkv * kD;
+  const uint32_t lane_off0 = (uint32_t)k0 * row_elems + hk * kD + 8 * dc;
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
     int base, nvalid;
     tile_rows(t, &base, &nvalid);
+    const int64_t r0 = (int64_t)kv0 + base;  // first key row of the tile
+    const int64_t lim = min((int64_t)nvalid, a.total_rows - r0);
+    const size_t tb = (r0 < a.total_rows) ? (size_t)r0 * row_elems : 0;
+    const uint16_t* kt = Kg + tb;
+    const uint16_t* vt = Vg + tb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = k0 + (j & 1) + 8 * (j >> 1);
-      const int64_t kr = (int64_t)kv0 + base + key;
-      const bool ok = key < nvalid && kr < a.total_rows;
-      // out-of-range keys read row 0 (always valid) and are zeroed
-      const size_t off = ((size_t)(ok ? kr : 0) * a.Hkv + hk) * kD + 8 * dc;
-      const uint4 kx = *reinterpret_cast<const uint4*>(Kg + off);
-      const uint4 vx = *reinterpret_cast<const uint4*>(Vg + off);
+      const int jk = (j & 1) + 8 * (j >> 1);
+      const bool ok = (int64_t)(k0 + jk) < lim;
+      // out-of-range keys read the tile's first row (or row 0) and are zeroed
+      const uint32_t off = ok ? lane_off0 + (uint32_t)jk * row_elems : (uint32_t)(hk * kD + 8 * dc);
+      const uint4 kx = *reinterpret_cast<const uint4*>(kt + off);
+      const uint4 vx = *reinterpret_cast<const uint4*>(vt + off);
       sk[j] = ok ? kx : make_uint4(0, 0, 0, 0);
       sv[j] = ok ? vx : make_uint4(0, 0, 0, 0);
     }
   };
-
-  // the key permutation of the S^T A operand: A row m -> key pi(m), chosen so
-  // that lane group gq's score registers v = 0..7 hold keys 8 gq + v and
-  // v = 8..15 hold keys 16 + 8 gq + (v - 8) of each 32-key block
-  const int m_a = lane & 31;
-  const int pi_m = 8 * ((m_a >> 2) & 1) + 16 * (m_a >> 4) + 4 * ((m_a >> 3) & 1) + (m_a & 3);
-
-  for (int t = t_begin; t < t_end; ++t) {
-    load_tile(t);
-    __syncthreads();
-    // K: 128-bit writes; V: transposed 32-bit writes of key pairs
+  // K: 128-bit writes; V: transposed 32-bit writes of key pairs
+  auto write_tile = [&](int bf) __attribute__((always_inline)) {
+    unsigned char* kl = k_lds[bf];
+    unsigned char* vl = v_lds[bf];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = k0 + (j & 1) + 8 * (j >> 1);
-      *reinterpret_cast<uint4*>(k_lds + k_lds_off(key, dc)) = sk[j];
+      *reinterpret_cast<uint4*>(kl + k_row_off(key) + 16 * dc) = sk[j];
     }
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp) {
@@ -180,10 +196,40 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int nsplit, in
         const uint32_t lo = (e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xFFFFu);
         const uint32_t hi = (e & 1) ? (bw[e >> 1] & 0xFFFF0000u) : (bw[e >> 1] << 16);
         const int dim = 8 * dc + e;
-        *reinterpret_cast<uint32_t*>(v_lds + v_lds_off(dim, key >> 3) + (key & 7) * 2) = lo | hi;
+        *reinterpret_cast<uint32_t*>(vl + v_lds_off(dim, key >> 3) + (key & 7) * 2) = lo | hi;
       }
     }
-    __syncthreads();
+  };
+
+  // the key permutation of the S^T A operand: A row m -> key pi(m), chosen so
+  // that lane group gq's score registers v = 0..7 hold keys 8 gq + v and
+  // v = 8..15 hold keys 16 + 8 gq + (v - 8) of each 32-key block
+  const int m_a = lane & 31;
+  const int pi_m = 8 * ((m_a >> 2) & 1) + 16 * (m_a >> 4) + 4 * ((m_a >> 3) & 1) + (m_a & 3);
+  const int kfrag0 = k_row_off(pi_m) + 16 * gq;  // + 32 ks, + kb block offset
+  // V^T fragment addresses for dims 32 db + n: the 4 chunk offsets of this
+  // lane; odd db flips swizzle bit 2, each db adds 32 dims * 128 bytes
+  int vfrag[4];
+  {
+    const int sw = (n ^ (n >> 3)) & 7;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int chunk = 4 * (c >> 1) + 2 * (c & 1) + gq;  // kb = c/2, hf = c%2
+      vfrag[c] = n * (kKeys * 2) + ((chunk ^ sw) << 4);
+    }
+  }
+
+  int bf = 0;
+  if (t_begin < t_end) {
+    load_tile(t_begin);
+    write_tile(0);
+  }
+  __syncthreads();
+  for (int t = t_begin; t < t_end; ++t) {
+    const bool has_next = t + 1 < t_end;
+    if (has_next) load_tile(t + 1);  // in flight while tile t is computed
+    const unsigned char* kl = k_lds[bf];
+    const unsigned char* vl = v_lds[bf];
 
     int base, nvalid;
     tile_rows(t, &base, &nvalid);
@@ -191,88 +237,85 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int nsplit, in
     uint64_t mword = 0;
     if (tree_tile && row_valid) mword = a.mask[((size_t)b * T + node) * W + (t - np)];
 
-    // ---- S^T = K Q^T for 2 blocks of 32 keys
-    floatx16 s[2];
+    // ---- two halves of 32 keys: S^T = K Q^T, online softmax, O^T += V^T P^T
+    const bool need_mask = tree_tile || nvalid < kKeys;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      floatx16 sc;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = 0.0f;
-      const int key = 32 * kb + pi_m;
+      for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(k_lds + k_lds_off(key, 2 * ks + gq));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + kfrag0 + kb * (32 * kKRow + 4 * 64) + 32 * ks);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
       }
-    }
-
-    // ---- mask, online softmax (log2 domain)
-    float tmax = -INFINITY;
+      // mask (tree tiles and the ragged last prefix tile only) and row max.
+      // Query rows past num_nodes need no masking: their scores never reach
+      // a valid row and their outputs are written as zeros.
+      float tmax = -INFINITY;
+      if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int v = 0; v < 16; ++v) {
+          const int kk = 32 * kb + 8 * gq + (v < 8 ? v : v + 8);
+          const bool ok = kk < nvalid && (!tree_tile || ((mword >> kk) & 1ull) != 0);
+          sc[v] = ok ? sc[v] : -INFINITY;
+          tmax = fmaxf(tmax, sc[v]);
+        }
+      } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = 32 * kb + 8 * gq + (v < 8 ? v : v + 8);
-        const bool ok =
-            row_valid && kk < nvalid && (!tree_tile || ((mword >> kk) & 1ull) != 0);
-        const float x = ok ? s[kb][v] : -INFINITY;
-        s[kb][v] = x;
-        tmax = fmaxf(tmax, x);
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
       }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax * c_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    // P is carried as a pair of bf16 MFMA operands, P = hi + lo with
-    // hi = bf16(p) and lo = bf16(p - hi): |p - hi - lo| <= 2^-18 p, so the
-    // weights keep ~fp32 accuracy even when only a few keys contribute.
-    float psum = 0.0f;
-    bf16x8 pf[2][2], pl[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax * c_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // P is carried as a pair of bf16 MFMA operands, P = hi + lo with
+      // hi = bf16(p) and lo = bf16(p - hi): |p - hi - lo| <= 2^-18 p, so the
+      // weights keep ~fp32 accuracy even when only a few keys contribute.
+      float psum = 0.0f;
+      bf16x8 pf[2], pl[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         bf16x2 hi2[4], lo2[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           floatx2 pr;
-          pr[0] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + 2 * e2], c_log2, -m_use));
-          pr[1] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + 2 * e2 + 1], c_log2, -m_use));
+          pr[0] = __builtin_amdgcn_exp2f(fmaf(sc[8 * hf + 2 * e2], c_log2, -m_use));
+          pr[1] = __builtin_amdgcn_exp2f(fmaf(sc[8 * hf + 2 * e2 + 1], c_log2, -m_use));
           psum += pr[0] + pr[1];
           hi2[e2] = __builtin_convertvector(pr, bf16x2);
           const uint32_t hb = __builtin_bit_cast(uint32_t, hi2[e2]);
           floatx2 rest = {pr[0] - __uint_as_float(hb << 16), pr[1] - __uint_as_float(hb & 0xFFFF0000u)};
           lo2[e2] = __builtin_convertvector(rest, bf16x2);
         }
-        pf[kb][hf] = bf16x8{hi2[0][0], hi2[0][1], hi2[1][0], hi2[1][1],
-                            hi2[2][0], hi2[2][1], hi2[3][0], hi2[3][1]};
-        pl[kb][hf] = bf16x8{lo2[0][0], lo2[0][1], lo2[1][0], lo2[1][1],
-                            lo2[2][0], lo2[2][1], lo2[3][0], lo2[3][1]};
+        pf[hf] = bf16x8{hi2[0][0], hi2[0][1], hi2[1][0], hi2[1][1],
+                        hi2[2][0], hi2[2][1], hi2[3][0], hi2[3][1]};
+        pl[hf] = bf16x8{lo2[0][0], lo2[0][1], lo2[1][0], lo2[1][1],
+                        lo2[2][0], lo2[2][1], lo2[3][0], lo2[3][1]};
       }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+      l_run = l_run * alpha + psum;
+      // the running max settles after a few tiles: rescale O only when it moved
+      if (__ballot(m_new != m_run) != 0) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-
-    // ---- O^T += V^T P^T
+          for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+      }
+      m_run = m_new;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int dim = 32 * db + (lane & 31);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int db = 0; db < 4; ++db) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(v_lds + v_lds_off(dim, 4 * kb + 2 * hf + gq));
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hf], acc_o[db], 0, 0, 0);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[kb][hf], acc_o[db], 0, 0, 0);
+          const int va = ((db & 1) ? (vfrag[2 * kb + hf] ^ 64) : vfrag[2 * kb + hf]) + db * 32 * kKeys * 2;
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + va);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hf], acc_o[db], 0, 0, 0);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[hf], acc_o[db], 0, 0, 0);
         }
       }
     }
+    if (has_next) write_tile(bf ^ 1);
+    __syncthreads();
+    bf ^= 1;
   }
 
   const float l_row = l_run + __shfl_xor(l_run, 32, 64);
@@ -299,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int nsplit, in
 
   // ---- split: write this split's partial (unnormalised O, m, l)
   const int Rpad = row_tiles * kTileRows;
-  const size_t bh = (size_t)b * a.Hkv + hk;
+  const size_t bh = (size_t)bhi;
   const size_t nbh = (size_t)a.batch * a.Hkv;
   {
     float* po = part_o + (((size_t)z * nbh + bh) * Rpad + row) * kD;
@@ -317,48 +360,72 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int nsplit, in
       pm[1] = l_row;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int ci = (int)(bh * row_tiles + xt);
-    const int old = atomicAdd(&counters[ci], 1);
-    s_last = (old == nsplit - 1) ? 1 : 0;
-    if (s_last) counters[ci] = 0;
+}
+
+// Merge of the split partials: 32 query rows of one (request, kv-head) per
+// workgroup. Per row, the split weights w_z = 2^(m_z - M) / sum_z 2^(m_z - M) l_z
+// go to LDS; then each output chunk sums w_z O_z with several partial loads
+// in flight per thread.
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int nsplit, int row_tiles,
+                                                      const float* part_o, const float* part_ml) {
+  constexpr int kRows = 32;
+  __shared__ float wts[kRows * 32];  // nsplit <= 32
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y / a.Hkv, hk = blockIdx.y - (blockIdx.y / a.Hkv) * a.Hkv;
+  const int g = a.Hq / a.Hkv;
+  const int T = a.T;
+  const int R = T * g;
+  const int nn = min(max(a.num_nodes[b], 0), T);
+  const int nvalid_rows = nn * g;
+  const int r0 = blockIdx.x * kRows;
+  const int Rpad = row_tiles * kTileRows;
+  const size_t bh = (size_t)b * a.Hkv + hk;
+  const size_t nbh = (size_t)a.batch * a.Hkv;
+  uint16_t* O = static_cast<uint16_t*>(a.out);
+  if (tid < kRows) {
+    const int rr = r0 + tid;
+    const size_t base = (bh * Rpad + rr) * 2;
+    const size_t zstride = nbh * Rpad * 2;
+    float M = -INFINITY;
+    for (int zz = 0; zz < nsplit; ++zz) M = fmaxf(M, part_ml[base + zz * zstride]);
+    float den = 0.f;
+    for (int zz = 0; zz < nsplit; ++zz) {
+      const float mz = part_ml[base + zz * zstride];
+      den += (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mz - M) * part_ml[base + zz * zstride + 1];
+    }
+    const float inv = (den > 0.f && rr < nvalid_rows) ? 1.0f / den : 0.0f;
+    for (int zz = 0; zz < nsplit; ++zz) {
+      const float mz = part_ml[base + zz * zstride];
+      wts[tid * nsplit + zz] = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mz - M) * inv;
+    }
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // ---- last split: merge all splits of these 128 rows
-  for (int idx = tid; idx < kTileRows * (kD / 4); idx += 256) {
+  constexpr int kU = 8;
+  for (int idx = tid; idx < kRows * (kD / 4); idx += 256) {
     const int rl = idx / (kD / 4), c4 = idx - rl * (kD / 4);
-    const int rr = tile_row0 + rl;
+    const int rr = r0 + rl;
     if (rr >= R) continue;
     const int nd = rr / g, hd = hk * g + (rr - nd * g);
-    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (rr < nvalid_rows) {
-      float M = -INFINITY;
-      for (int zz = 0; zz < nsplit; ++zz)
-        M = fmaxf(M, part_ml[(((size_t)zz * nbh + bh) * Rpad + rr) * 2]);
-      if (M != -INFINITY) {
-        float den = 0.f;
-        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int zz = 0; zz < nsplit; ++zz) {
-          const size_t pr = ((size_t)zz * nbh + bh) * Rpad + rr;
-          const float mz = part_ml[pr * 2];
-          const float wz = __builtin_amdgcn_exp2f(mz - M);  // 0 for an empty split
-          den += wz * part_ml[pr * 2 + 1];
-          const float4 oz = *reinterpret_cast<const float4*>(part_o + pr * kD + 4 * c4);
-          num.x += wz * oz.x;
-          num.y += wz * oz.y;
-          num.z += wz * oz.z;
-          num.w += wz * oz.w;
-        }
-        const float inv = den > 0.f ? 1.0f / den : 0.0f;
-        res = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    const size_t pbase = (bh * Rpad + rr) * kD + 4 * c4;
+    const size_t pstride = nbh * Rpad * kD;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z0 = 0; z0 < nsplit; z0 += kU) {
+      float4 oz[kU];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const int zz = min(z0 + j, nsplit - 1);
+        oz[j] = *reinterpret_cast<const float4*>(part_o + pbase + zz * pstride);
+      }
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const float wz = (z0 + j < nsplit) ? wts[rl * nsplit + z0 + j] : 0.f;
+        acc.x += wz * oz[j].x;
+        acc.y += wz * oz[j].y;
+        acc.z += wz * oz[j].z;
+        acc.w += wz * oz[j].w;
       }
     }
-    floatx2 lo2 = {res.x, res.y}, hi2 = {res.z, res.w};
+    floatx2 lo2 = {acc.x, acc.y}, hi2 = {acc.z, acc.w};
     bf16x2 l2 = __builtin_convertvector(lo2, bf16x2);
     bf16x2 h2 = __builtin_convertvector(hi2, bf16x2);
     bf16x4 o4 = {l2[0], l2[1], h2[0], h2[1]};
@@ -435,19 +502,51 @@ __global__ __launch_bounds__(128) void k_attn_simple(AttnArgs a) {
   }
 }
 
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    hipDeviceProp_t prop;
+    cus[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+                   ? prop.multiProcessorCount
+                   : 256;
+  }
+  return cus[dev];
+}
+
+// Split of each row tile's key range across workgroups: pick the count that
+// minimises a simple time model -- rounds of resident workgroups (two per
+// CU) times the key tiles per workgroup, plus the partial-result traffic of
+// the merge -- with at least 4 key tiles per split.
 AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int max_prefix_len) {
-  AttnSplit s{1, 0};
+  AttnSplit s{1, 0, 0, 0};
   if (dtype != 0 || D != kD) return s;
   const int g = Hq / Hkv;
   const int R = T * g;
   s.row_tiles = (R + kTileRows - 1) / kTileRows;
   const long blocks = (long)batch * Hkv * s.row_tiles;
   const int tiles = (max_prefix_len + kKeys - 1) / kKeys + (T + kKeys - 1) / kKeys;
-  const long target = 512;
-  int ns = (int)((target + blocks - 1) / blocks);
-  ns = std::min(ns, std::max(1, tiles / 4));
-  ns = std::max(1, std::min(ns, 32));
-  s.nsplit = ns;
+  const long slots = 2L * device_cus();
+  const double t_tile_us = 1.0, t_fixed_us = 3.0, hbm_bytes_per_us = 8.0e6;
+  int best = 1;
+  double best_t = 1e300;
+  for (int ns = 1; ns <= 32; ++ns) {
+    if (ns > 1 && tiles < 4 * ns) break;
+    const long wgs = blocks * ns;
+    const long rounds = (wgs + slots - 1) / slots;
+    const int per = (tiles + ns - 1) / ns;
+    double t = rounds * (per * t_tile_us + t_fixed_us);
+    if (ns > 1) t += t_fixed_us + 2.0 * (double)wgs * kTileRows * kD * 4 / hbm_bytes_per_us;
+    if (t < best_t * 0.97) {
+      best_t = t;
+      best = ns;
+    }
+  }
+  s.nsplit = best;
+  s.total = (int)(blocks * best);
+  s.per_xcd = (s.total + kXcds - 1) / kXcds;
   return s;
 }
 
@@ -470,8 +569,7 @@ size_t attn_workspace_bytes(int dtype, int batch, int T, int Hq, int Hkv, int D,
   const AttnSplit s = plan_split(dtype, batch, T, Hq, Hkv, D, max_prefix_len);
   if (s.nsplit <= 1) return 256;
   const size_t rows = (size_t)s.nsplit * batch * Hkv * s.row_tiles * kTileRows;
-  return align_up(rows * kD * 4, 256) + align_up(rows * 2 * 4, 256) +
-         align_up((size_t)batch * Hkv * s.row_tiles * 4, 256);
+  return align_up(rows * kD * 4, 256) + align_up(rows * 2 * 4, 256);
 }
 
 hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
@@ -480,19 +578,21 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   const AttnSplit s = plan_split(a.dtype, a.batch, a.T, a.Hq, a.Hkv, a.D, a.max_prefix_len);
   float* part_o = nullptr;
   float* part_ml = nullptr;
-  int32_t* counters = nullptr;
   if (s.nsplit > 1) {
     const size_t rows = (size_t)s.nsplit * a.batch * a.Hkv * s.row_tiles * kTileRows;
     char* p = static_cast<char*>(ws);
     part_o = reinterpret_cast<float*>(p);
     p += align_up(rows * kD * 4, 256);
     part_ml = reinterpret_cast<float*>(p);
-    p += align_up(rows * 2 * 4, 256);
-    counters = reinterpret_cast<int32_t*>(p);
   }
-  dim3 grid(s.row_tiles, a.batch * a.Hkv, s.nsplit), block(256);
-  hipLaunchKernelGGL(k_attn_mfma, grid, block, 0, st, a, s.nsplit, s.row_tiles, part_o, part_ml,
-                     counters);
+  dim3 grid(s.per_xcd * kXcds), block(256);
+  hipLaunchKernelGGL(k_attn_mfma, grid, block, 0, st, a, s, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s.nsplit <= 1) return e;
+  const int R = a.T * (a.Hq / a.Hkv);
+  dim3 cgrid((R + 31) / 32, a.batch * a.Hkv);
+  hipLaunchKernelGGL(k_attn_combine, cgrid, block, 0, st, a, s.nsplit, s.row_tiles,
+                     (const float*)part_o, (const float*)part_ml);
   return hipGetLastError();
 }
 

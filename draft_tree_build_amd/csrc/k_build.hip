@@ -1,16 +1,16 @@
-// Draft-tree build on gfx950: per-position log-softmax + top-K, best-first
-// tree, ancestor bitmask -- one kernel launch.
+// Draft-tree build on gfx950: per-position log-softmax + top-K (k_rows), then
+// the best-first tree and its ancestor bitmask (k_tree).
 //
 // Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees"
 // (Ringel, Romano), summary page, cited as [BDDT <section>].
 //
-// Grid: one workgroup per drafter row (request b, position i). Each workgroup
-// streams its row from HBM once (kept in registers when it fits), computes the
-// row maximum, the K best tokens and the exact fixed-point softmax
-// normaliser, and writes the K candidates with their log-probabilities. The
-// last workgroup of a request to finish (arrival counter in the workspace)
-// then builds that request's tree with one wavefront and writes the tree
-// arrays and the ancestor mask. No host round trip, no second launch.
+// k_rows: one workgroup per drafter row (request b, position i). Each
+// workgroup streams its row from HBM once (kept in registers when it fits),
+// computes the row maximum, the K best tokens and the exact fixed-point
+// softmax normaliser, and writes the K candidates with their log-probs.
+// k_tree: one workgroup per request; one wavefront runs the N pops with the
+// frontier in registers and a DPP butterfly for the wave-wide minimum, then
+// the whole workgroup writes the tree arrays and the mask.
 #include "ddtree_device.h"
 #include "ddtree_internal.h"
 
@@ -34,10 +34,6 @@ struct TreeShared {
   int32_t npar[kMaxT];
   int32_t ndep[kMaxT];
   float nscore[kMaxT];
-};
-union BuildShared {
-  RowShared row;
-  TreeShared tree;
 };
 
 // ------------------------------------------------------------------ input views
@@ -237,71 +233,237 @@ __device__ __forceinline__ uint64_t tree_key(float score, int depth, int parent,
   return ((uint64_t)hi << 32) | lo;
 }
 
+// 64-bit DPP move within rows of 16 lanes (all lanes read a valid source).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Minimum over the wave of a 32-bit value, returned uniformly: butterfly
+// within each row of 16 lanes (quad_perm 1032, quad_perm 2301, half-row
+// mirror, row mirror -- each a v_min_u32 with a DPP operand), then the four
+// row minima through readlane.
+__device__ __forceinline__ uint32_t wave_min32_uniform(uint32_t v) {
+  v = min(v, dpp32<0xB1>(v));
+  v = min(v, dpp32<0x4E>(v));
+  v = min(v, dpp32<0x141>(v));
+  v = min(v, dpp32<0x140>(v));
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t c = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return min(a, c);
+}
+// Wave-wide minimum of a 64-bit key, returned uniformly: the high words
+// (scores) first; the low words only decide between lanes that tie on them.
+__device__ __forceinline__ uint64_t wave_min_uniform(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t hmin = wave_min32_uniform(hi);
+  const uint64_t tied = __ballot(hi == hmin);
+  uint32_t lmin;
+  if (__builtin_popcountll(tied) == 1) {
+    lmin = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__builtin_ctzll(tied));
+  } else {
+    lmin = wave_min32_uniform(hi == hmin ? lo : 0xFFFFFFFFu);
+  }
+  return ((uint64_t)hmin << 32) | lmin;
+}
+
 // Best-first tree of one request, run by one wavefront  [BDDT §4.3, App. A].
 // Every popped node p keeps exactly one pending candidate, its next
-// unpopped child; it lives in register slot p/64 of lane p%64. A pop is a
-// wave-wide minimum over those keys; the popped candidate (parent p, depth d,
-// rank r) becomes node n, p's slot advances to rank r+1 (next sibling) and
-// n's slot takes n's best child. Returns num_nodes (root included).
+// unpopped child; it lives in register slot p/64 of lane p%64 (S slots per
+// lane cover nodes 0..64S-1). A pop is a wave-wide minimum over those keys;
+// the popped candidate (parent p, depth d, rank r) becomes node n, p's slot
+// advances to rank r+1 (next sibling) and n's slot takes n's best child.
+//
+// Each slot also carries what its candidate's successors need: the parent's
+// score, the log-prob of the next rank at the same position (sibling) and the
+// log-prob of the best token one position deeper (child). The pop's critical
+// path thus reads no LDS: the table reads for the two new candidates are
+// issued in one pop and consumed after the next pop's wave reduction.
+// Node records hold the rank; tokens are looked up after the loop.
+// Returns num_nodes (root included).
+template <int S>
 __device__ int tree_wave(TreeShared& sh, int L, int K, int N, int root_token) {
   const int lane = threadIdx.x & 63;
-  const int S = (N + 1 + 63) >> 6;
-  uint64_t fk[kSlots];
+  uint64_t fk[S];
+  float fps[S], fln[S], fcl[S];
 #pragma unroll
-  for (int s = 0; s < kSlots; ++s) fk[s] = kEmpty;
+  for (int s = 0; s < S; ++s) {
+    fk[s] = kEmpty;
+    fps[s] = 0.0f;
+    fln[s] = 0.0f;
+    fcl[s] = 0.0f;
+  }
   if (lane == 0) {
-    sh.ntok[0] = root_token;
+    sh.ntok[0] = 0;
     sh.npar[0] = -1;
     sh.ndep[0] = 0;
     sh.nscore[0] = 0.0f;
     fk[0] = tree_key(0.0f + sh.lp[0], 1, 0, 0);
+    fln[0] = sh.lp[min(1, K - 1)];
+    fcl[0] = sh.lp[min(1, L - 1) * K];
   }
+  int pend_p = -1, pend_n = -1;  // slots whose successor fields are in flight
+  float pA = 0.0f, pB = 0.0f, pC = 0.0f;
   int n = 1;
   for (; n <= N; ++n) {
     uint64_t lb = fk[0];
 #pragma unroll
-    for (int s = 1; s < kSlots; ++s)
-      if (s < S) lb = fk[s] < lb ? fk[s] : lb;
-    const uint64_t best = wave_min(lb);
+    for (int s = 1; s < S; ++s) lb = umin64(lb, fk[s]);
+    const uint64_t best = wave_min_uniform(lb);
+    // the previous pop's table reads have landed during the reduction
+    if (pend_p >= 0) {
+      const int pps = pend_p >> 6, ppl = pend_p & 63, pns = pend_n >> 6, pnl = pend_n & 63;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        if (s == pps && lane == ppl) fln[s] = pA;
+        if (s == pns && lane == pnl) {
+          fln[s] = pB;
+          fcl[s] = pC;
+        }
+      }
+    }
     if (best == kEmpty) break;
     const uint32_t hi = (uint32_t)(best >> 32), lo = (uint32_t)best;
     const float score = order_to_float(~hi);
     const int d = (int)(lo >> 25);
     const int p = (int)((lo >> 14) & 0x7FFu);
     const int r = (int)((lo >> 9) & 31u);
-    const int tok = sh.tok[(d - 1) * K + r];
-    const float score_p = sh.nscore[p];
-    uint64_t kp = kEmpty, kn = kEmpty;
-    if (r + 1 < K) kp = tree_key(score_p + sh.lp[(d - 1) * K + r + 1], d, p, r + 1);
-    if (d + 1 <= L) kn = tree_key(score + sh.lp[d * K], d + 1, n, 0);
+    const int ps = p >> 6, pl = p & 63, ns = n >> 6, nl = n & 63;
+    float w_ps = 0.0f, w_ln = 0.0f, w_cl = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (s == ps) {
+        w_ps = fps[s];
+        w_ln = fln[s];
+        w_cl = fcl[s];
+      }
+    }
+    const float child_lp0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w_cl), pl));
+    // branch-free: a missing sibling / child gets the all-ones (empty) key
+    const uint64_t kp = tree_key(w_ps + w_ln, d, p, r + 1) | (0ull - (uint64_t)(r + 1 >= K));
+    const uint64_t kn = tree_key(score + child_lp0, d + 1, n, 0) | (0ull - (uint64_t)(d >= L));
     if (lane == 0) {
-      sh.ntok[n] = tok;
+      sh.ntok[n] = r;  // rank; replaced by the token after the loop
       sh.npar[n] = p;
       sh.ndep[n] = d;
       sh.nscore[n] = score;
     }
-    const int ps = p >> 6, pl = p & 63, ns = n >> 6, nl = n & 63;
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
+    for (int s = 0; s < S; ++s) {
       if (s == ps && lane == pl) fk[s] = kp;
-      if (s == ns && lane == nl) fk[s] = kn;
+      if (s == ns && lane == nl) {
+        fk[s] = kn;
+        fps[s] = score;
+      }
+    }
+    // successor fields of the two new candidates (clamped indices; a value is
+    // only used when the corresponding rank / depth exists)
+    pA = sh.lp[(d - 1) * K + min(r + 2, K - 1)];
+    pB = sh.lp[min(d, L - 1) * K + min(1, K - 1)];
+    pC = sh.lp[min(d + 1, L - 1) * K];
+    pend_p = p;
+    pend_n = n;
+  }
+  if (lane == 0) sh.ntok[0] = root_token;
+  for (int i = 1 + lane; i < n; i += 64) sh.ntok[i] = sh.tok[(sh.ndep[i] - 1) * K + sh.ntok[i]];
+  return n;
+}
+
+struct TreeArgs {
+  const int32_t* topk_tok;
+  const float* topk_lp;
+  const int32_t* row_flags;
+  const int32_t* root_tokens;
+  int L, K, N;
+  int32_t* tokens;
+  int32_t* parents;
+  int32_t* depths;
+  float* scores;
+  int32_t* num_nodes;
+  uint64_t* mask;
+  int32_t* status;
+};
+
+// One workgroup per request: tree (wave 0), then outputs and mask.
+template <int S>
+__global__ __launch_bounds__(256) void k_tree(TreeArgs a) {
+  __shared__ TreeShared tr;
+  __shared__ int s_nn;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.x;
+  const int K = a.K;
+  const int LK = a.L * K;
+  for (int i = tid; i < LK; i += 256) {
+    tr.tok[i] = a.topk_tok[(size_t)b * LK + i];
+    tr.lp[i] = a.topk_lp[(size_t)b * LK + i];
+  }
+  if (wid == 1 && a.status) {  // L <= 64 row flags, one per lane, OR-reduced
+    int f = lane < a.L ? a.row_flags[(size_t)b * a.L + lane] : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, 64);
+    if (lane == 0) a.status[b] = f;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const int nn = tree_wave<S>(tr, a.L, K, a.N, a.root_tokens[b]);
+    if (lane == 0) s_nn = nn;
+  }
+  __syncthreads();
+  const int nn = s_nn;
+  const int T = a.N + 1;
+  for (int i = tid; i < T; i += 256) {
+    const size_t o = (size_t)b * T + i;
+    const bool ok = i < nn;
+    a.tokens[o] = ok ? tr.ntok[i] : -1;
+    a.parents[o] = ok ? tr.npar[i] : -1;
+    a.depths[o] = ok ? tr.ndep[i] : -1;
+    a.scores[o] = ok ? tr.nscore[i] : -INFINITY;
+  }
+  if (tid == 0) a.num_nodes[b] = nn;
+  if (a.mask) {
+    // one thread per row: a single walk up the ancestor chain, whose node
+    // indices decrease, emits the row's words from the highest to the lowest
+    const int W = (T + 63) >> 6;
+    for (int i = tid; i < T; i += 256) {
+      uint64_t* out = a.mask + ((size_t)b * T + i) * W;
+      int j = i < nn ? i : -1;
+      for (int w = W - 1; w >= 0; --w) {
+        uint64_t bits = 0;
+        while (j >= 64 * w) {
+          bits |= 1ull << (j - 64 * w);
+          j = tr.npar[j];
+        }
+        out[w] = bits;
+      }
     }
   }
-  return n;
 }
 
 // ------------------------------------------------------------------ the kernel
 template <typename IN_T, int BLOCK, int CH, bool GENERAL>
-__global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
-  __shared__ BuildShared sm;
+__global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a) {
+  __shared__ RowShared sm_row;
   __shared__ float red_f[16];
   __shared__ int red_i[16];
   __shared__ uint64_t red_u[16];
   __shared__ int s_cnt;
   __shared__ uint32_t s_t0;
   __shared__ float s_lse;
-  __shared__ int s_last;
-  __shared__ int s_nn;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.x;
@@ -347,11 +509,11 @@ __global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
     uint32_t w = __shfl_xor(tkey, o, 64);
     tkey = w > tkey ? w : tkey;
   }
-  if ((tid % G) == 0) sm.row.gmax[tid / G] = tkey;
+  if ((tid % G) == 0) sm_row.gmax[tid / G] = tkey;
   if (tid == 0) s_cnt = 0;
   __syncthreads();
   if (wid == 0) {
-    uint32_t v = sm.row.gmax[lane];
+    uint32_t v = sm_row.gmax[lane];
     for (int k = 2; k <= 64; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
         uint32_t o = __shfl_xor(v, j, 64);
@@ -383,7 +545,7 @@ __global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
     const uint32_t kk = float_order(xs);
     if (kk >= t0) {
       const int s = atomicAdd(&s_cnt, 1);
-      if (s < kCandMax) sm.row.cand[s] = cand_word(kk, id);
+      if (s < kCandMax) sm_row.cand[s] = cand_word(kk, id);
     }
     float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
     d = finite_m ? d : -INFINITY;
@@ -412,7 +574,7 @@ __global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
     __syncthreads();
     view.visit_mem(tid, [&](int id, float raw) __attribute__((always_inline)) {
       uint32_t kk = key_of(raw);
-      if (kk > t) sm.row.cand[atomicAdd(&s_cnt, 1)] = cand_word(kk, id);
+      if (kk > t) sm_row.cand[atomicAdd(&s_cnt, 1)] = cand_word(kk, id);
     });
     const int need = K - ngt;
     int base = 0;
@@ -425,7 +587,7 @@ __global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
       int j = 0;
       view.visit_chunk(c, tid, [&](int id, float raw) __attribute__((always_inline)) {
         if (key_of(raw) == t) {
-          if (base + excl + j < need) sm.row.cand[atomicAdd(&s_cnt, 1)] = cand_word(t, id);
+          if (base + excl + j < need) sm_row.cand[atomicAdd(&s_cnt, 1)] = cand_word(t, id);
           ++j;
         }
       });
@@ -436,9 +598,9 @@ __global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
   }
   int P = 2;
   while (P < nsort) P <<= 1;
-  for (int i = nsort + tid; i < P; i += BLOCK) sm.row.cand[i] = 0;
+  for (int i = nsort + tid; i < P; i += BLOCK) sm_row.cand[i] = 0;
   __syncthreads();
-  bitonic_desc<BLOCK>(sm.row.cand, P);
+  bitonic_desc<BLOCK>(sm_row.cand, P);
 
   const uint64_t S = block_sum_u64<BLOCK>((uint64_t)acc, red_u);
   if (tid == 0) s_lse = (m == -INFINITY) ? INFINITY : lse_from_fixed(S);
@@ -446,7 +608,7 @@ __global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
 
   // ---- the K candidates with their log-probabilities
   if (tid < K) {
-    const uint64_t c = sm.row.cand[tid];
+    const uint64_t c = sm_row.cand[tid];
     const uint32_t kk = (uint32_t)(c >> 32);
     const int id = (int)(0xFFFFFFFFu - (uint32_t)c);
     const float x = order_to_float(kk);
@@ -462,61 +624,6 @@ __global__ __launch_bounds__(BLOCK) void k_build(BuildArgs a) {
   }
   if (tid == 0) a.row_flags[r] = flags;
 
-  // ---- arrival: the last row of request b builds its tree
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = atomicAdd(&a.counters[b], 1);
-    s_last = (old == a.L - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) a.counters[b] = 0;
-
-  TreeShared& tr = sm.tree;
-  const int LK = a.L * K;
-  for (int i = tid; i < LK; i += BLOCK) {
-    tr.tok[i] = a.topk_tok[(size_t)b * LK + i];
-    tr.lp[i] = a.topk_lp[(size_t)b * LK + i];
-  }
-  if (tid == 0 && a.status) {
-    int f = 0;
-    for (int i = 0; i < a.L; ++i) f |= a.row_flags[(size_t)b * a.L + i];
-    a.status[b] = f;
-  }
-  __syncthreads();
-  if (wid == 0) {
-    const int nn = tree_wave(tr, a.L, K, a.N, a.root_tokens[b]);
-    if (lane == 0) s_nn = nn;
-  }
-  __syncthreads();
-  const int nn = s_nn;
-  const int T = a.N + 1;
-  for (int i = tid; i < T; i += BLOCK) {
-    const size_t o = (size_t)b * T + i;
-    const bool ok = i < nn;
-    a.tokens[o] = ok ? tr.ntok[i] : -1;
-    a.parents[o] = ok ? tr.npar[i] : -1;
-    a.depths[o] = ok ? tr.ndep[i] : -1;
-    a.scores[o] = ok ? tr.nscore[i] : -INFINITY;
-  }
-  if (tid == 0) a.num_nodes[b] = nn;
-  if (a.mask) {
-    const int W = (T + 63) >> 6;
-    for (int idx = tid; idx < T * W; idx += BLOCK) {
-      const int i = idx / W, w = idx - (idx / W) * W;
-      uint64_t bits = 0;
-      if (i < nn) {
-        int j = i;
-        while (j >= 64 * w) {
-          if (j < 64 * (w + 1)) bits |= 1ull << (j - 64 * w);
-          j = tr.npar[j];
-        }
-      }
-      a.mask[((size_t)b * T + i) * W + w] = bits;
-    }
-  }
 }
 
 // Standalone ancestor mask of given trees [BDDT Abstract, §4.1].
@@ -548,13 +655,13 @@ template <typename IN_T, int BLOCK, int CH>
 hipError_t launch_t(const BuildArgs& a, hipStream_t st) {
   dim3 grid(a.batch * a.L), block(BLOCK);
   if (a.mode == 0) {
-    hipLaunchKernelGGL((k_build<IN_T, BLOCK, CH, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, CH, false>), grid, block, 0, st, a);
   } else if constexpr (CH > 16) {
     // temperature scaling / argmax mode on the longest rows: the streaming
     // variant (the register-resident one does not fit without spilling)
-    hipLaunchKernelGGL((k_build<IN_T, BLOCK, 0, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, 0, true>), grid, block, 0, st, a);
   } else {
-    hipLaunchKernelGGL((k_build<IN_T, BLOCK, CH, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, CH, true>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -580,12 +687,11 @@ hipError_t launch_dt(const BuildArgs& a, hipStream_t st) {
 
 size_t build_workspace_bytes(int batch, int L, int K) {
   size_t n = (size_t)batch * L * K;
-  return align_up(n * 4, 256) * 2 + align_up((size_t)batch * L * 4, 256) +
-         align_up((size_t)batch * 4, 256);
+  return align_up(n * 4, 256) * 2 + align_up((size_t)batch * L * 4, 256);
 }
 
 void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** topk_lp,
-                 int32_t** row_flags, int32_t** counters) {
+                 int32_t** row_flags) {
   char* p = static_cast<char*>(ws);
   size_t n = (size_t)batch * L * K;
   *topk_tok = reinterpret_cast<int32_t*>(p);
@@ -593,13 +699,30 @@ void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** 
   *topk_lp = reinterpret_cast<float*>(p);
   p += align_up(n * 4, 256);
   *row_flags = reinterpret_cast<int32_t*>(p);
-  p += align_up((size_t)batch * L * 4, 256);
-  *counters = reinterpret_cast<int32_t*>(p);
 }
 
+namespace {
+template <int S>
+hipError_t launch_tree_s(const TreeArgs& t, int batch, hipStream_t st) {
+  hipLaunchKernelGGL((k_tree<S>), dim3(batch), dim3(256), 0, st, t);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_build(const BuildArgs& a, hipStream_t st) {
-  if (a.dtype == 0) return launch_dt<uint16_t>(a, st);
-  return launch_dt<float>(a, st);
+  hipError_t e = (a.dtype == 0) ? launch_dt<uint16_t>(a, st) : launch_dt<float>(a, st);
+  if (e != hipSuccess) return e;
+  TreeArgs t{a.topk_tok, a.topk_lp, a.row_flags, a.root_tokens, a.L, a.K, a.N,
+             a.tokens, a.parents, a.depths, a.scores, a.num_nodes, a.mask, a.status};
+  // frontier slots per lane: nodes 0..N live in lanes n % 64, slots n / 64
+  const int S = (a.N + 1 + 63) / 64;
+  if (S <= 1) return launch_tree_s<1>(t, a.batch, st);
+  if (S <= 2) return launch_tree_s<2>(t, a.batch, st);
+  if (S <= 3) return launch_tree_s<3>(t, a.batch, st);
+  if (S <= 4) return launch_tree_s<4>(t, a.batch, st);
+  if (S <= 5) return launch_tree_s<5>(t, a.batch, st);
+  if (S <= 9) return launch_tree_s<9>(t, a.batch, st);
+  return launch_tree_s<kSlots>(t, a.batch, st);
 }
 
 hipError_t launch_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,

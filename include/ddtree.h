@@ -16,9 +16,9 @@
  *    checks run on the host before anything is enqueued: a call that fails
  *    them launches nothing and writes nothing. DDTREE_ERR_HIP reports a
  *    failed launch.
- *  - Workspaces hold per-call scratch plus small arrival counters. A new
- *    workspace must be zero-filled once before its first use (e.g.
- *    torch.zeros); every call leaves the counters at zero again. A workspace
+ *  - Workspaces hold per-call scratch only (staged top-K tables, per-split
+ *    attention partials, per-node target ids); no contents carry from one
+ *    call to the next, so a workspace needs no initialisation. A workspace
  *    serves one call at a time: calls that overlap on one workspace race.
  *  - dtype: DDTREE_BF16 (bfloat16 storage) or DDTREE_F32 (float32 storage).
  */
@@ -90,7 +90,7 @@ const char *ddtree_strerror(int status);
  *   topk_tokens   [batch, L, K] int32 or NULL        out
  *   topk_logprobs [batch, L, K] float32 or NULL      out
  *   status_flags  [batch] int32 or NULL              out (DDTREE_STATUS_*)
- *   workspace     >= ddtree_build_workspace_size(...) bytes, zeroed once
+ *   workspace     >= ddtree_build_workspace_size(...) bytes
  *
  * Limits: 1 <= batch; 1 <= L <= 64; 1 <= K <= min(32, V); 1 <= N <= 1024;
  * V <= 2^19; draft_temp >= 0 and finite.
@@ -134,7 +134,7 @@ int ddtree_mask(const int32_t *parents, const int32_t *num_nodes, int batch, int
  *   max_prefix_len  an upper bound on every P_b (sizes the work split)
  *   total_rows    number of rows of k and v (bounds checking)
  *   softmax_scale <= 0 selects 1/sqrt(D)
- *   workspace     >= ddtree_verify_workspace_size(...) bytes, zeroed once
+ *   workspace     >= ddtree_verify_workspace_size(...) bytes
  *
  * bf16: fp32 accumulation on MFMA, bf16 output. f32: fp32 throughout.
  * Limits: Hq % Hkv == 0; T <= 1025; D in {32, 64, 128} (bf16: D = 128).
@@ -165,7 +165,7 @@ int ddtree_verify_attn(const void *q, const void *k, const void *v, ddtree_dtype
  *   bonus           [batch] int32                         out
  *   target_argmax   [batch, T] int32 or NULL              out: the target token
  *                   per node (-1 for rows >= num_nodes[b])
- *   workspace       >= ddtree_accept_workspace_size(...) bytes, zeroed once
+ *   workspace       >= ddtree_accept_workspace_size(...) bytes
  * Limits: T <= 1025, 1 <= L <= 64, V <= 2^31 - 1 (logits path: V >= 1).
  */
 size_t ddtree_accept_workspace_size(int batch, int T);

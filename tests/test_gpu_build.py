@@ -84,7 +84,7 @@ def test_build_limits(L, K, N):
 
 
 def test_build_repeatable_on_one_workspace():
-    """Two calls on one workspace: the arrival counters are left at zero."""
+    """Two calls on one workspace give identical results."""
     x = _logits(4, 8, 2000, seed=3)
     ws = api.new_workspace(api.ddtree_build_workspace_size(4, 8, 2000, 8, 40), DEV)
     note("build twice on one workspace")
@@ -92,10 +92,6 @@ def test_build_repeatable_on_one_workspace():
     g2, _ = gpu_build(x, [0, 1, 2, 3], 8, 40, 1.0, ws=ws)
     for k in g1:
         np.testing.assert_array_equal(g1[k], g2[k])
-    n = 4 * 8 * 8
-    al = lambda x: (x + 255) // 256 * 256
-    off = al(4 * n) * 2 + al(4 * 4 * 8)
-    assert not ws[off:off + 16].cpu().any()  # the four arrival counters are back at zero
     o = oracle.build_tree(x, [0, 1, 2, 3], 8, 40, 1.0)
     assert_same_build(g2, o)
 
