@@ -31,6 +31,22 @@ void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** 
                  int32_t** row_flags);
 hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
 
+struct TreeArgs {
+  const int32_t* topk_tok;  // [batch, L, K]
+  const float* topk_lp;
+  const int32_t* row_flags; // [batch, L]
+  const int32_t* root_tokens;
+  int L, K, N;
+  int32_t* tokens;
+  int32_t* parents;
+  int32_t* depths;
+  float* scores;
+  int32_t* num_nodes;
+  uint64_t* mask;           // may be null
+  int32_t* status;          // may be null
+};
+hipError_t launch_tree(const TreeArgs& t, int batch, hipStream_t stream);
+
 hipError_t launch_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,
                        uint64_t* mask, hipStream_t stream);
 

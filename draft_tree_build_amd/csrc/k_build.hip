@@ -1,5 +1,5 @@
-// Draft-tree build on gfx950: per-position log-softmax + top-K (k_rows), then
-// the best-first tree and its ancestor bitmask (k_tree).
+// Draft-tree build on gfx950: per-position log-softmax + top-K (k_rows); the
+// best-first tree and its ancestor bitmask follow in k_tree (k_tree.hip).
 //
 // Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees"
 // (Ringel, Romano), summary page, cited as [BDDT <section>].
@@ -8,9 +8,6 @@
 // workgroup streams its row from HBM once (kept in registers when it fits),
 // computes the row maximum, the K best tokens and the exact fixed-point
 // softmax normaliser, and writes the K candidates with their log-probs.
-// k_tree: one workgroup per request; one wavefront runs the N pops with the
-// frontier in registers and a DPP butterfly for the wave-wide minimum, then
-// the whole workgroup writes the tree arrays and the mask.
 #include "ddtree_device.h"
 #include "ddtree_internal.h"
 
@@ -18,22 +15,11 @@ namespace ddt {
 namespace {
 
 constexpr int kCandMax = 2048;   // candidate buffer for the top-K sort (LDS)
-constexpr int kSlots = 17;       // frontier slots per lane: ceil((1024 + 1) / 64)
-constexpr uint64_t kEmpty = ~0ull;
-constexpr int kMaxLK = 64 * 32;
 constexpr int kMaxT = 1025;
 
 struct RowShared {
   uint64_t cand[kCandMax];
   uint32_t gmax[64];
-};
-struct TreeShared {
-  int32_t tok[kMaxLK];
-  float lp[kMaxLK];
-  int32_t ntok[kMaxT];
-  int32_t npar[kMaxT];
-  int32_t ndep[kMaxT];
-  float nscore[kMaxT];
 };
 
 // ------------------------------------------------------------------ input views
@@ -223,235 +209,6 @@ __device__ void bitonic_desc(uint64_t* s, int P) {
 // Candidate word for the top-K sort: larger = better = (x desc, id asc).
 __device__ __forceinline__ uint64_t cand_word(uint32_t key, int id) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
-}
-
-// ------------------------------------------------------------------ tree keys
-// Frontier key, smaller = popped first: score desc, depth, parent, rank asc.
-__device__ __forceinline__ uint64_t tree_key(float score, int depth, int parent, int rank) {
-  uint32_t hi = ~float_order(score);
-  uint32_t lo = ((uint32_t)depth << 25) | ((uint32_t)parent << 14) | ((uint32_t)rank << 9);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// 64-bit DPP move within rows of 16 lanes (all lanes read a valid source).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi =
-      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-// Minimum over the wave of a 32-bit value, returned uniformly: butterfly
-// within each row of 16 lanes (quad_perm 1032, quad_perm 2301, half-row
-// mirror, row mirror -- each a v_min_u32 with a DPP operand), then the four
-// row minima through readlane.
-__device__ __forceinline__ uint32_t wave_min32_uniform(uint32_t v) {
-  v = min(v, dpp32<0xB1>(v));
-  v = min(v, dpp32<0x4E>(v));
-  v = min(v, dpp32<0x141>(v));
-  v = min(v, dpp32<0x140>(v));
-  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
-                         (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
-  const uint32_t c = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
-                         (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
-  return min(a, c);
-}
-// Wave-wide minimum of a 64-bit key, returned uniformly: the high words
-// (scores) first; the low words only decide between lanes that tie on them.
-__device__ __forceinline__ uint64_t wave_min_uniform(uint64_t v) {
-  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-  const uint32_t hmin = wave_min32_uniform(hi);
-  const uint64_t tied = __ballot(hi == hmin);
-  uint32_t lmin;
-  if (__builtin_popcountll(tied) == 1) {
-    lmin = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__builtin_ctzll(tied));
-  } else {
-    lmin = wave_min32_uniform(hi == hmin ? lo : 0xFFFFFFFFu);
-  }
-  return ((uint64_t)hmin << 32) | lmin;
-}
-
-// Best-first tree of one request, run by one wavefront  [BDDT §4.3, App. A].
-// Every popped node p keeps exactly one pending candidate, its next
-// unpopped child; it lives in register slot p/64 of lane p%64 (S slots per
-// lane cover nodes 0..64S-1). A pop is a wave-wide minimum over those keys;
-// the popped candidate (parent p, depth d, rank r) becomes node n, p's slot
-// advances to rank r+1 (next sibling) and n's slot takes n's best child.
-//
-// Each slot also carries what its candidate's successors need: the parent's
-// score, the log-prob of the next rank at the same position (sibling) and the
-// log-prob of the best token one position deeper (child). The pop's critical
-// path thus reads no LDS: the table reads for the two new candidates are
-// issued in one pop and consumed after the next pop's wave reduction.
-// Node records hold the rank; tokens are looked up after the loop.
-// Returns num_nodes (root included).
-template <int S>
-__device__ int tree_wave(TreeShared& sh, int L, int K, int N, int root_token) {
-  const int lane = threadIdx.x & 63;
-  uint64_t fk[S];
-  float fps[S], fln[S], fcl[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    fk[s] = kEmpty;
-    fps[s] = 0.0f;
-    fln[s] = 0.0f;
-    fcl[s] = 0.0f;
-  }
-  if (lane == 0) {
-    sh.ntok[0] = 0;
-    sh.npar[0] = -1;
-    sh.ndep[0] = 0;
-    sh.nscore[0] = 0.0f;
-    fk[0] = tree_key(0.0f + sh.lp[0], 1, 0, 0);
-    fln[0] = sh.lp[min(1, K - 1)];
-    fcl[0] = sh.lp[min(1, L - 1) * K];
-  }
-  int pend_p = -1, pend_n = -1;  // slots whose successor fields are in flight
-  float pA = 0.0f, pB = 0.0f, pC = 0.0f;
-  int n = 1;
-  for (; n <= N; ++n) {
-    uint64_t lb = fk[0];
-#pragma unroll
-    for (int s = 1; s < S; ++s) lb = umin64(lb, fk[s]);
-    const uint64_t best = wave_min_uniform(lb);
-    // the previous pop's table reads have landed during the reduction
-    if (pend_p >= 0) {
-      const int pps = pend_p >> 6, ppl = pend_p & 63, pns = pend_n >> 6, pnl = pend_n & 63;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        if (s == pps && lane == ppl) fln[s] = pA;
-        if (s == pns && lane == pnl) {
-          fln[s] = pB;
-          fcl[s] = pC;
-        }
-      }
-    }
-    if (best == kEmpty) break;
-    const uint32_t hi = (uint32_t)(best >> 32), lo = (uint32_t)best;
-    const float score = order_to_float(~hi);
-    const int d = (int)(lo >> 25);
-    const int p = (int)((lo >> 14) & 0x7FFu);
-    const int r = (int)((lo >> 9) & 31u);
-    const int ps = p >> 6, pl = p & 63, ns = n >> 6, nl = n & 63;
-    float w_ps = 0.0f, w_ln = 0.0f, w_cl = 0.0f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s == ps) {
-        w_ps = fps[s];
-        w_ln = fln[s];
-        w_cl = fcl[s];
-      }
-    }
-    const float child_lp0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w_cl), pl));
-    // branch-free: a missing sibling / child gets the all-ones (empty) key
-    const uint64_t kp = tree_key(w_ps + w_ln, d, p, r + 1) | (0ull - (uint64_t)(r + 1 >= K));
-    const uint64_t kn = tree_key(score + child_lp0, d + 1, n, 0) | (0ull - (uint64_t)(d >= L));
-    if (lane == 0) {
-      sh.ntok[n] = r;  // rank; replaced by the token after the loop
-      sh.npar[n] = p;
-      sh.ndep[n] = d;
-      sh.nscore[n] = score;
-    }
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      if (s == ps && lane == pl) fk[s] = kp;
-      if (s == ns && lane == nl) {
-        fk[s] = kn;
-        fps[s] = score;
-      }
-    }
-    // successor fields of the two new candidates (clamped indices; a value is
-    // only used when the corresponding rank / depth exists)
-    pA = sh.lp[(d - 1) * K + min(r + 2, K - 1)];
-    pB = sh.lp[min(d, L - 1) * K + min(1, K - 1)];
-    pC = sh.lp[min(d + 1, L - 1) * K];
-    pend_p = p;
-    pend_n = n;
-  }
-  if (lane == 0) sh.ntok[0] = root_token;
-  for (int i = 1 + lane; i < n; i += 64) sh.ntok[i] = sh.tok[(sh.ndep[i] - 1) * K + sh.ntok[i]];
-  return n;
-}
-
-struct TreeArgs {
-  const int32_t* topk_tok;
-  const float* topk_lp;
-  const int32_t* row_flags;
-  const int32_t* root_tokens;
-  int L, K, N;
-  int32_t* tokens;
-  int32_t* parents;
-  int32_t* depths;
-  float* scores;
-  int32_t* num_nodes;
-  uint64_t* mask;
-  int32_t* status;
-};
-
-// One workgroup per request: tree (wave 0), then outputs and mask.
-template <int S>
-__global__ __launch_bounds__(256) void k_tree(TreeArgs a) {
-  __shared__ TreeShared tr;
-  __shared__ int s_nn;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int b = blockIdx.x;
-  const int K = a.K;
-  const int LK = a.L * K;
-  for (int i = tid; i < LK; i += 256) {
-    tr.tok[i] = a.topk_tok[(size_t)b * LK + i];
-    tr.lp[i] = a.topk_lp[(size_t)b * LK + i];
-  }
-  if (wid == 1 && a.status) {  // L <= 64 row flags, one per lane, OR-reduced
-    int f = lane < a.L ? a.row_flags[(size_t)b * a.L + lane] : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, 64);
-    if (lane == 0) a.status[b] = f;
-  }
-  __syncthreads();
-  if (wid == 0) {
-    const int nn = tree_wave<S>(tr, a.L, K, a.N, a.root_tokens[b]);
-    if (lane == 0) s_nn = nn;
-  }
-  __syncthreads();
-  const int nn = s_nn;
-  const int T = a.N + 1;
-  for (int i = tid; i < T; i += 256) {
-    const size_t o = (size_t)b * T + i;
-    const bool ok = i < nn;
-    a.tokens[o] = ok ? tr.ntok[i] : -1;
-    a.parents[o] = ok ? tr.npar[i] : -1;
-    a.depths[o] = ok ? tr.ndep[i] : -1;
-    a.scores[o] = ok ? tr.nscore[i] : -INFINITY;
-  }
-  if (tid == 0) a.num_nodes[b] = nn;
-  if (a.mask) {
-    // one thread per row: a single walk up the ancestor chain, whose node
-    // indices decrease, emits the row's words from the highest to the lowest
-    const int W = (T + 63) >> 6;
-    for (int i = tid; i < T; i += 256) {
-      uint64_t* out = a.mask + ((size_t)b * T + i) * W;
-      int j = i < nn ? i : -1;
-      for (int w = W - 1; w >= 0; --w) {
-        uint64_t bits = 0;
-        while (j >= 64 * w) {
-          bits |= 1ull << (j - 64 * w);
-          j = tr.npar[j];
-        }
-        out[w] = bits;
-      }
-    }
-  }
 }
 
 // ------------------------------------------------------------------ the kernel
@@ -701,28 +458,13 @@ void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** 
   *row_flags = reinterpret_cast<int32_t*>(p);
 }
 
-namespace {
-template <int S>
-hipError_t launch_tree_s(const TreeArgs& t, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((k_tree<S>), dim3(batch), dim3(256), 0, st, t);
-  return hipGetLastError();
-}
-}  // namespace
 
 hipError_t launch_build(const BuildArgs& a, hipStream_t st) {
   hipError_t e = (a.dtype == 0) ? launch_dt<uint16_t>(a, st) : launch_dt<float>(a, st);
   if (e != hipSuccess) return e;
   TreeArgs t{a.topk_tok, a.topk_lp, a.row_flags, a.root_tokens, a.L, a.K, a.N,
              a.tokens, a.parents, a.depths, a.scores, a.num_nodes, a.mask, a.status};
-  // frontier slots per lane: nodes 0..N live in lanes n % 64, slots n / 64
-  const int S = (a.N + 1 + 63) / 64;
-  if (S <= 1) return launch_tree_s<1>(t, a.batch, st);
-  if (S <= 2) return launch_tree_s<2>(t, a.batch, st);
-  if (S <= 3) return launch_tree_s<3>(t, a.batch, st);
-  if (S <= 4) return launch_tree_s<4>(t, a.batch, st);
-  if (S <= 5) return launch_tree_s<5>(t, a.batch, st);
-  if (S <= 9) return launch_tree_s<9>(t, a.batch, st);
-  return launch_tree_s<kSlots>(t, a.batch, st);
+  return launch_tree(t, a.batch, st);
 }
 
 hipError_t launch_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,

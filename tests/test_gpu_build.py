@@ -125,3 +125,63 @@ def test_mask_matches_oracle():
         got = mask.cpu().numpy().view(np.uint64)
         for b in range(B):
             np.testing.assert_array_equal(got[b], oracle.mask(par[b], nn[b], T))
+
+
+def _lane_refills(lp, L, K, N, lanes=64):
+    """How often a 64-entry sorted candidate window runs dry while overflow
+    candidates remain, replayed on the oracle's own tables (the test below
+    uses it only to make sure its inputs reach that case)."""
+    def key(score, d, p, r):
+        return (-float(score), d, p, r)
+    scores = [np.float32(0)]
+    s0 = np.float32(np.float32(0) + lp[0][0])
+    head, over, n, refills = [(key(s0, 1, 0, 0), s0, 1, 0, 0)], [], 1, 0
+    while n <= N:
+        if not head:
+            if not over:
+                break
+            refills += 1
+            over.sort()
+            head, over = over[:lanes], over[lanes:]
+        _, s, d, p, r = head.pop(0)
+        scores.append(s)
+        new = []
+        if r + 1 < K:
+            v = np.float32(scores[p] + lp[d - 1][r + 1])
+            new.append((key(v, d, p, r + 1), v, d, p, r + 1))
+        if d < L:
+            v = np.float32(s + lp[d][0])
+            new.append((key(v, d + 1, n, 0), v, d + 1, n, 0))
+        if len(head) >= N - n:
+            over = []
+        for c in new:
+            if over and c >= min(over):
+                over.append(c)
+            else:
+                head.append(c)
+                head.sort()
+                if len(head) > lanes:
+                    over.append(head.pop())
+        if len(head) >= N - n:
+            over = []
+        n += 1
+    return refills
+
+
+@pytest.mark.parametrize("L,K,spread", [(16, 8, 3.0), (64, 4, 3.0), (4, 32, 3.0), (16, 8, 0.0)])
+def test_build_overflow_refills(L, K, spread):
+    """Budgets far beyond 64 with widely spread log-probs: the candidate
+    window of the tree kernel runs dry and is refilled from its overflow list."""
+    B, V, N = 2, 64, 1024
+    rng = np.random.default_rng(L * K)
+    x = np.full((B, L, V), -60.0, np.float32)
+    for b in range(B):
+        for i in range(L):
+            gaps = rng.exponential(spread, K) if spread else np.zeros(K)
+            x[b, i, rng.permutation(V)[:K]] = -np.cumsum(gaps)
+    x = torch.from_numpy(x)
+    o = oracle.build_tree(x, [5, 6], K, N, 1.0)
+    assert sum(_lane_refills(o["topk_lp"][b], L, K, N) for b in range(B)) > 0
+    note("build overflow L=%d K=%d spread=%g" % (L, K, spread))
+    g, _ = gpu_build(x, [5, 6], K, N, 1.0)
+    assert_same_build(g, o)
