@@ -83,6 +83,10 @@ def load_traffic(workload, stage):
     return ent.get("bytes_per_launch")
 
 
+def graphs_off(args):
+    return not args.graphs
+
+
 def cpu_baseline(w, inputs, nodes_per_step, budget_s):
     """The oracle, single-threaded, on whole rounds of the same workload."""
     import numpy as np
@@ -171,55 +175,65 @@ def main():
     num_nodes = rnd.num_nodes.cpu()
     nodes_per_step = int((num_nodes - 1).sum())
 
-    # One HIP graph per (input copy, stage): the three ABI calls of a round
-    # replay without host launch overhead; events between the graph launches
-    # time each stage inside the timed region.
-    graphs = None
+    # Per input copy, one HIP graph holding the whole round and one graph per
+    # stage. Most timed steps replay the whole-round graph (no host launch
+    # overhead between the ABI calls). Every SAMPLE_EVERY-th step replays the
+    # stage graphs instead, with HIP events between them on the same stream:
+    # those events time each stage inside the timed region. --no-graphs
+    # launches the calls eagerly, every step with events.
+    SAMPLE_EVERY = 20
+    whole, per_stage = None, None
     if args.graphs:
-        log("capturing %d x 3 graphs" % R)
+        log("capturing %d x 4 graphs" % R)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        graphs = []
+        whole, per_stage = [], []
         with torch.cuda.stream(side):
             for c in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for f in stages:
+                        f(copies[c])
+                whole.append(g)
                 row = []
                 for f in stages:
                     g = torch.cuda.CUDAGraph()
                     with torch.cuda.graph(g, stream=side):
                         f(copies[c])
                     row.append(g)
-                graphs.append(row)
+                per_stage.append(row)
         torch.cuda.current_stream().wait_stream(side)
         for i in range(min(R, args.warmup)):
-            for g in graphs[i]:
+            whole[i].replay()
+            for g in per_stage[i]:
                 g.replay()
         torch.cuda.synchronize()
 
-    def step(i, ev):
-        c = i % R
-        ev[0].record()
-        for k in range(3):
-            if graphs is not None:
-                graphs[c][k].replay()
-            else:
-                stages[k](copies[c])
-            ev[k + 1].record()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    log("timing %d steps" % args.steps)
+    sampled = [i for i in range(args.steps)
+               if graphs_off(args) or i % SAMPLE_EVERY == SAMPLE_EVERY - 1] or [args.steps - 1]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    log("timing %d steps (%d with stage events)" % (args.steps, len(sampled)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        c = i % R
+        ev = evs.get(i)
+        if ev is None:
+            whole[c].replay()
+            continue
+        ev[0].record()
+        for k in range(3):
+            if per_stage is not None:
+                per_stage[c][k].replay()
+            else:
+                stages[k](copies[c])
+            ev[k + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_ms = {"build": 0.0, "verify": 0.0, "accept": 0.0}
-    for ev in evs:
-        stage_ms["build"] += ev[0].elapsed_time(ev[1])
-        stage_ms["verify"] += ev[1].elapsed_time(ev[2])
-        stage_ms["accept"] += ev[2].elapsed_time(ev[3])
-    stage_us = {k: v * 1e3 / args.steps for k, v in stage_ms.items()}
+    stage_us = {}
+    for k, name in enumerate(("build", "verify", "accept")):
+        stage_us[name] = sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in sampled) * 1e3 / len(sampled)
     value = nodes_per_step / (ms_per_step * 1e-3)
     log("ms/step %.4f  stages(us) %s" % (ms_per_step, {k: round(v, 2) for k, v in stage_us.items()}))
 
@@ -261,7 +275,8 @@ def main():
                 "Q/K/V ~N(0,1))",
         "config": {"workload": w.name, "batch": w.batch, "L": w.L, "V": w.V, "K": w.K, "N": w.N,
                    "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                   "draft_temp": tau, "input_copies": R, "hip_graphs": bool(args.graphs)},
+                   "draft_temp": tau, "input_copies": R, "hip_graphs": bool(args.graphs),
+                   "stage_event_steps": len(sampled)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -33,10 +33,9 @@ const char* ddtree_strerror(int status) {
 }
 
 size_t ddtree_build_workspace_size(int batch, int L, int V, int K, int N) {
-  (void)V;
   (void)N;
-  if (batch < 1 || L < 1 || K < 1) return 0;
-  return build_workspace_bytes(batch, L, K);
+  if (batch < 1 || L < 1 || K < 1 || V < 1 || K > DDTREE_MAX_K) return 0;
+  return build_workspace_bytes(batch, L, V, K);
 }
 
 int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens, int batch,
@@ -53,7 +52,7 @@ int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens
   if (L > DDTREE_MAX_L || K > DDTREE_MAX_K || N > DDTREE_MAX_N || V > DDTREE_MAX_V)
     return DDTREE_ERR_UNSUPPORTED;
   if ((long long)batch * L > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
-  const size_t need = build_workspace_bytes(batch, L, K);
+  const size_t need = build_workspace_bytes(batch, L, V, K);
   if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
 
   BuildArgs a{};
@@ -79,13 +78,9 @@ int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens
   a.num_nodes = num_nodes;
   a.mask = mask;
   a.status = status_flags;
-  int32_t *ws_tok, *ws_flags;
-  float* ws_lp;
-  build_carve(workspace, batch, L, K, &ws_tok, &ws_lp, &ws_flags);
-  a.topk_tok = topk_tokens ? topk_tokens : ws_tok;
-  a.topk_lp = topk_logprobs ? topk_logprobs : ws_lp;
-  a.row_flags = ws_flags;
-  return hip_status(launch_build(a, static_cast<hipStream_t>(stream)));
+  a.topk_tok = topk_tokens;
+  a.topk_lp = topk_logprobs;
+  return hip_status(launch_build(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 int ddtree_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,

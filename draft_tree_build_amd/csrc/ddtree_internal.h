@@ -21,20 +21,38 @@ struct BuildArgs {
   float* scores;
   int32_t* num_nodes;
   uint64_t* mask;           // may be null
-  int32_t* topk_tok;        // [batch, L, K] (caller output or workspace)
-  float* topk_lp;
+  int32_t* topk_tok;        // [batch, L, K] or null
+  float* topk_lp;           // [batch, L, K] or null
   int32_t* status;          // may be null
-  int32_t* row_flags;       // workspace [batch, L]
+  // workspace: per-row results of the row stage
+  uint64_t* row_cand;       // [rows, K] candidate words, best first
+  uint64_t* row_sum;        // [rows, S] fixed-point partial sums
+  float* row_max;           // [rows]
+  int32_t* row_flags;       // [rows]
+  // workspace: per-chunk results of split rows (S > 1)
+  uint64_t* part_cand;      // [rows, S, K]
+  float* part_max;          // [rows, S]
+  int32_t* part_flags;      // [rows, S]
 };
-size_t build_workspace_bytes(int batch, int L, int K);
-void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** topk_lp,
-                 int32_t** row_flags);
-hipError_t launch_build(const BuildArgs& a, hipStream_t stream);
+struct RowPlan {
+  int S;        // chunks per row (1: no split)
+  int cv;       // 16-byte vectors per chunk
+  bool vec_ok;  // rows are 16-byte aligned
+};
+RowPlan plan_rows(int batch, int L, int V, int K, int esize, bool vec_ok);
+size_t build_workspace_bytes(int batch, int L, int V, int K);
+// Workspace layout for S chunks per row; fills the workspace pointers of `a`
+// when ws and a are given. Returns the bytes needed.
+size_t build_layout(int batch, int L, int K, int S, void* ws, BuildArgs* a);
+hipError_t launch_build(BuildArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 
 struct TreeArgs {
-  const int32_t* topk_tok;  // [batch, L, K]
-  const float* topk_lp;
-  const int32_t* row_flags; // [batch, L]
+  const uint64_t* row_cand; // [batch * L, K]
+  const uint64_t* row_sum;  // [batch * L, S]
+  const float* row_max;
+  const int32_t* row_flags;
+  int S;
+  int mode;
   const int32_t* root_tokens;
   int L, K, N;
   int32_t* tokens;
@@ -43,6 +61,8 @@ struct TreeArgs {
   float* scores;
   int32_t* num_nodes;
   uint64_t* mask;           // may be null
+  int32_t* topk_tok;        // may be null
+  float* topk_lp;           // may be null
   int32_t* status;          // may be null
 };
 hipError_t launch_tree(const TreeArgs& t, int batch, hipStream_t stream);

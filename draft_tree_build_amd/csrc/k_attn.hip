@@ -219,23 +219,32 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     }
   }
 
+  // mask word of this lane's query row for tree tile t (prefetched with the tile)
+  const uint64_t* mrow = a.mask + ((size_t)b * T + node) * W;
+  auto load_mword = [&](int t) __attribute__((always_inline)) -> uint64_t {
+    return (t >= np && row_valid) ? mrow[t - np] : 0ull;
+  };
   int bf = 0;
+  uint64_t mword_next = 0;
   if (t_begin < t_end) {
     load_tile(t_begin);
+    mword_next = load_mword(t_begin);
     write_tile(0);
   }
   __syncthreads();
   for (int t = t_begin; t < t_end; ++t) {
     const bool has_next = t + 1 < t_end;
-    if (has_next) load_tile(t + 1);  // in flight while tile t is computed
+    const uint64_t mword = mword_next;
+    if (has_next) {  // in flight while tile t is computed
+      load_tile(t + 1);
+      mword_next = load_mword(t + 1);
+    }
     const unsigned char* kl = k_lds[bf];
     const unsigned char* vl = v_lds[bf];
 
     int base, nvalid;
     tile_rows(t, &base, &nvalid);
     const bool tree_tile = t >= np;
-    uint64_t mword = 0;
-    if (tree_tile && row_valid) mword = a.mask[((size_t)b * T + node) * W + (t - np)];
 
     // ---- two halves of 32 keys: S^T = K Q^T, online softmax, O^T += V^T P^T
     const bool need_mask = tree_tile || nvalid < kKeys;
@@ -382,22 +391,26 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int nsplit, in
   const size_t bh = (size_t)b * a.Hkv + hk;
   const size_t nbh = (size_t)a.batch * a.Hkv;
   uint16_t* O = static_cast<uint16_t*>(a.out);
+  // split maxima and sums of the 32 rows, all loads in flight at once
+  __shared__ float sm[kRows * 32], sl[kRows * 32];
+  const size_t zstride = nbh * Rpad * 2;
+  for (int idx = tid; idx < kRows * nsplit; idx += 256) {
+    const int rl = idx / nsplit, zz = idx - rl * nsplit;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (bh * Rpad + r0 + rl) * 2 + zz * zstride);
+    sm[idx] = ml.x;
+    sl[idx] = ml.y;
+  }
+  __syncthreads();
   if (tid < kRows) {
     const int rr = r0 + tid;
-    const size_t base = (bh * Rpad + rr) * 2;
-    const size_t zstride = nbh * Rpad * 2;
     float M = -INFINITY;
-    for (int zz = 0; zz < nsplit; ++zz) M = fmaxf(M, part_ml[base + zz * zstride]);
+    for (int zz = 0; zz < nsplit; ++zz) M = fmaxf(M, sm[tid * nsplit + zz]);
     float den = 0.f;
-    for (int zz = 0; zz < nsplit; ++zz) {
-      const float mz = part_ml[base + zz * zstride];
-      den += (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mz - M) * part_ml[base + zz * zstride + 1];
-    }
+    for (int zz = 0; zz < nsplit; ++zz)
+      den += (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[tid * nsplit + zz] - M) * sl[tid * nsplit + zz];
     const float inv = (den > 0.f && rr < nvalid_rows) ? 1.0f / den : 0.0f;
-    for (int zz = 0; zz < nsplit; ++zz) {
-      const float mz = part_ml[base + zz * zstride];
-      wts[tid * nsplit + zz] = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mz - M) * inv;
-    }
+    for (int zz = 0; zz < nsplit; ++zz)
+      wts[tid * nsplit + zz] = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[tid * nsplit + zz] - M) * inv;
   }
   __syncthreads();
   constexpr int kU = 8;

@@ -4,10 +4,15 @@
 // Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees"
 // (Ringel, Romano), summary page, cited as [BDDT <section>].
 //
-// k_rows: one workgroup per drafter row (request b, position i). Each
-// workgroup streams its row from HBM once (kept in registers when it fits),
-// computes the row maximum, the K best tokens and the exact fixed-point
-// softmax normaliser, and writes the K candidates with their log-probs.
+// k_rows: one workgroup per drafter row (request b, position i), or, when
+// there are too few rows to fill the chip, one per chunk of a row (k_rows
+// with PART, then k_rows_sum). A workgroup streams its row (chunk) from HBM
+// once, kept in registers when it fits, and produces the row maximum, the K
+// best tokens as candidate words (ranking key, id) and the exact fixed-point
+// softmax normaliser (as partial sums, exact in any order). k_tree turns
+// these into log-probabilities.
+#include <algorithm>
+
 #include "ddtree_device.h"
 #include "ddtree_internal.h"
 
@@ -59,9 +64,10 @@ struct Elem<float> {
 template <typename IN_T, int BLOCK, int CH>
 struct RowView {
   static constexpr int EPV = Elem<IN_T>::kPerVec;
-  const IN_T* row;
-  int V;
+  const IN_T* row;  // first element of the row (chunk)
+  int V;            // elements in the row (chunk)
   int nvec;
+  int id0;          // token id of element 0
   uint4 reg[CH > 0 ? CH : 1];
 
   __device__ __forceinline__ void load(int tid) {
@@ -96,10 +102,10 @@ struct RowView {
   __device__ __forceinline__ void visit_chunk(int c, int tid, F&& f) const {
     if constexpr (CH >= 0) {
       int vi = c * BLOCK + tid;
-      if (vi < nvec) Elem<IN_T>::unpack(reinterpret_cast<const uint4*>(row)[vi], vi * EPV, f);
+      if (vi < nvec) Elem<IN_T>::unpack(reinterpret_cast<const uint4*>(row)[vi], id0 + vi * EPV, f);
     } else {
       int v = c * BLOCK + tid;
-      if (v < V) f(v, Elem<IN_T>::scalar(row, v));
+      if (v < V) f(id0 + v, Elem<IN_T>::scalar(row, v));
     }
   }
   template <class F>
@@ -113,7 +119,7 @@ struct RowView {
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         int vi = c * BLOCK + tid;
-        if (vi < nvec) Elem<IN_T>::unpack(reg[c], vi * EPV, f);
+        if (vi < nvec) Elem<IN_T>::unpack(reg[c], id0 + vi * EPV, f);
       }
     } else {
       const int nc = num_chunks();
@@ -211,28 +217,41 @@ __device__ __forceinline__ uint64_t cand_word(uint32_t key, int id) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-// ------------------------------------------------------------------ the kernel
-template <typename IN_T, int BLOCK, int CH, bool GENERAL>
-__global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a) {
+// ------------------------------------------------------------------ the kernels
+// PART = false: one workgroup per row; writes the row's K best candidate
+// words (sorted, best first), its maximum, status bits and fixed-point sum.
+// PART = true: one workgroup per chunk s of row r (S chunks of cv vectors);
+// writes the chunk's K best words, maximum and status bits; k_rows_sum then
+// adds the chunk sums and merges the chunk candidates.
+template <typename IN_T, int BLOCK, int CH, bool GENERAL, bool PART>
+__global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a, RowPlan pl) {
   __shared__ RowShared sm_row;
   __shared__ float red_f[16];
   __shared__ int red_i[16];
   __shared__ uint64_t red_u[16];
   __shared__ int s_cnt;
   __shared__ uint32_t s_t0;
-  __shared__ float s_lse;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int r = blockIdx.x;
-  const int b = r / a.L;
+  const int r = PART ? (int)blockIdx.x / pl.S : (int)blockIdx.x;
+  const int sidx = PART ? (int)blockIdx.x - r * pl.S : 0;
   const int K = a.K;
   const int mode = GENERAL ? a.mode : 0;
   const float inv_tau = a.inv_tau;
 
-  RowView<IN_T, BLOCK, CH> view;
+  using View = RowView<IN_T, BLOCK, CH>;
+  View view;
   view.row = reinterpret_cast<const IN_T*>(a.logits) + (size_t)r * a.V;
   view.V = a.V;
-  view.nvec = a.V / RowView<IN_T, BLOCK, CH>::EPV;
+  view.nvec = a.V / View::EPV;
+  view.id0 = 0;
+  if (PART) {
+    const int v0 = sidx * pl.cv;
+    view.nvec = min(pl.cv, view.nvec - v0);
+    view.V = view.nvec * View::EPV;
+    view.id0 = v0 * View::EPV;
+    view.row += view.id0;
+  }
   view.load(tid);
 
   auto xval = [&](float raw) __attribute__((always_inline)) -> float {  // ranking value before sanitising
@@ -241,7 +260,7 @@ __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a) {
     return x;
   };
 
-  // ---- pass 1: row maximum, non-finite flag, per-thread maximum key
+  // ---- pass 1: maximum, non-finite flag, per-thread maximum key
   float tmax = -INFINITY;
   int tflag = 0;
   bool has = false;
@@ -255,7 +274,6 @@ __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a) {
   });
   const float m = block_max<BLOCK>(tmax, red_f);
   int flags = block_or<BLOCK>(tflag, red_i);
-  if (m == -INFINITY) flags |= 2;
 
   // ---- a lower bound t0 for the K-th largest key: the K-th largest of 64
   //      group maxima (each is a distinct element of the row)
@@ -291,8 +309,8 @@ __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a) {
     return float_order(x);
   };
 
-  // ---- pass 2, fused: candidates (every element with key >= t0) and the
-  //      exact fixed-point normaliser S = sum_v rint(2^44 E(x_v - m))
+  // ---- pass 2: candidates (every element with key >= t0); without a split
+  //      also the exact fixed-point normaliser S = sum_v rint(2^44 E(x_v - m))
   double acc = 0.0;
   const bool finite_m = m != -INFINITY;
   view.fence();
@@ -301,12 +319,14 @@ __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a) {
     const float xs = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
     const uint32_t kk = float_order(xs);
     if (kk >= t0) {
-      const int s = atomicAdd(&s_cnt, 1);
-      if (s < kCandMax) sm_row.cand[s] = cand_word(kk, id);
+      const int c = atomicAdd(&s_cnt, 1);
+      if (c < kCandMax) sm_row.cand[c] = cand_word(kk, id);
     }
-    float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
-    d = finite_m ? d : -INFINITY;
-    acc += exp_fixed(d);
+    if (!PART) {
+      float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
+      d = finite_m ? d : -INFINITY;
+      acc += exp_fixed(d);
+    }
   });
   __syncthreads();
   const int ncand = s_cnt;
@@ -354,33 +374,97 @@ __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a) {
     nsort = K;
   }
   int P = 2;
-  while (P < nsort) P <<= 1;
-  for (int i = nsort + tid; i < P; i += BLOCK) sm_row.cand[i] = 0;
+  while (P < max(nsort, K)) P <<= 1;
+  for (int i = nsort + tid; i < P; i += BLOCK) sm_row.cand[i] = 0;  // 0: below every real word
   __syncthreads();
   bitonic_desc<BLOCK>(sm_row.cand, P);
 
-  const uint64_t S = block_sum_u64<BLOCK>((uint64_t)acc, red_u);
-  if (tid == 0) s_lse = (m == -INFINITY) ? INFINITY : lse_from_fixed(S);
-  __syncthreads();
-
-  // ---- the K candidates with their log-probabilities
-  if (tid < K) {
-    const uint64_t c = sm_row.cand[tid];
-    const uint32_t kk = (uint32_t)(c >> 32);
-    const int id = (int)(0xFFFFFFFFu - (uint32_t)c);
-    const float x = order_to_float(kk);
-    float lp;
-    if (m == -INFINITY) {
-      lp = -INFINITY;
-    } else {
-      float d = (GENERAL && mode == 2) ? ((x == m) ? 0.0f : -INFINITY) : (x - m);
-      lp = d - s_lse;
+  // ---- outputs
+  if (PART) {
+    const int q = r * pl.S + sidx;
+    if (tid < K) a.part_cand[(size_t)q * K + tid] = sm_row.cand[tid];
+    if (tid == 0) {
+      a.part_max[q] = m;
+      a.part_flags[q] = flags;
     }
-    a.topk_tok[(size_t)r * K + tid] = id;
-    a.topk_lp[(size_t)r * K + tid] = lp;
+  } else {
+    const uint64_t S = block_sum_u64<BLOCK>((uint64_t)acc, red_u);
+    if (tid < K) a.row_cand[(size_t)r * K + tid] = sm_row.cand[tid];
+    if (tid == 0) {
+      a.row_max[r] = m;
+      a.row_flags[r] = flags | (m == -INFINITY ? 2 : 0);
+      a.row_sum[r] = S;
+    }
   }
-  if (tid == 0) a.row_flags[r] = flags;
+}
 
+// Second pass of a split row: the fixed-point sum of chunk s with the row
+// maximum over all chunks; the workgroup of chunk 0 also merges the chunks'
+// candidate words into the row's K best.
+template <typename IN_T, int BLOCK, int CH, bool GENERAL>
+__global__ __launch_bounds__(BLOCK) void k_rows_sum(BuildArgs a, RowPlan pl) {
+  __shared__ uint64_t red_u[16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r = (int)blockIdx.x / pl.S;
+  const int sidx = (int)blockIdx.x - r * pl.S;
+  const int K = a.K;
+  const int mode = GENERAL ? a.mode : 0;
+  const float inv_tau = a.inv_tau;
+
+  using View = RowView<IN_T, BLOCK, CH>;
+  View view;
+  const int v0 = sidx * pl.cv;
+  view.nvec = min(pl.cv, a.V / View::EPV - v0);
+  view.V = view.nvec * View::EPV;
+  view.id0 = v0 * View::EPV;
+  view.row = reinterpret_cast<const IN_T*>(a.logits) + (size_t)r * a.V + view.id0;
+  view.load(tid);
+
+  // row maximum and status bits over the S chunks (S <= 64: one load per lane)
+  const int q0 = r * pl.S;
+  const float mc = lane < pl.S ? a.part_max[q0 + lane] : -INFINITY;
+  const float m = wave_max(mc);
+
+  double acc = 0.0;
+  const bool finite_m = m != -INFINITY;
+  view.visit(tid, [&](int, float raw) __attribute__((always_inline)) {
+    float x = raw;
+    if (GENERAL && mode == 1) x = x * inv_tau;
+    const float xs = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
+    float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
+    d = finite_m ? d : -INFINITY;
+    acc += exp_fixed(d);
+  });
+  const uint64_t S = block_sum_u64<BLOCK>((uint64_t)acc, red_u);
+  if (tid == 0) a.row_sum[(size_t)q0 + sidx] = S;
+
+  if (sidx != 0 || wid != 0) return;
+  // merge: the K best of the S x K chunk words, by repeated wave maxima
+  int fl = lane < pl.S ? a.part_flags[q0 + lane] : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+  constexpr int kMaxPer = 8;  // S * K <= 512
+  const int nw = pl.S * K;
+  uint64_t wv[kMaxPer];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int i = lane + 64 * j;
+    wv[j] = i < nw ? a.part_cand[(size_t)q0 * K + i] : 0ull;
+  }
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = wv[0];
+#pragma unroll
+    for (int j = 1; j < kMaxPer; ++j) best = wv[j] > best ? wv[j] : best;
+    const uint64_t top = wave_max(best);
+    // words are distinct (ids differ), unless both are padding (0)
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) wv[j] = (wv[j] == top && top != 0ull) ? 0ull : wv[j];
+    if (lane == 0) a.row_cand[(size_t)r * K + k] = top;
+  }
+  if (lane == 0) {
+    a.row_max[r] = m;
+    a.row_flags[r] = fl | (m == -INFINITY ? 2 : 0);
+  }
 }
 
 // Standalone ancestor mask of given trees [BDDT Abstract, §4.1].
@@ -409,61 +493,138 @@ __global__ __launch_bounds__(256) void k_mask(const int32_t* parents, const int3
 }
 
 template <typename IN_T, int BLOCK, int CH>
-hipError_t launch_t(const BuildArgs& a, hipStream_t st) {
+hipError_t launch_t(const BuildArgs& a, RowPlan pl, hipStream_t st) {
   dim3 grid(a.batch * a.L), block(BLOCK);
   if (a.mode == 0) {
-    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, CH, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, CH, false, false>), grid, block, 0, st, a, pl);
   } else if constexpr (CH > 16) {
     // temperature scaling / argmax mode on the longest rows: the streaming
     // variant (the register-resident one does not fit without spilling)
-    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, 0, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, 0, true, false>), grid, block, 0, st, a, pl);
   } else {
-    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, CH, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_rows<IN_T, BLOCK, CH, true, false>), grid, block, 0, st, a, pl);
+  }
+  return hipGetLastError();
+}
+
+// Split rows: 256 threads per chunk, the chunk's vectors in registers.
+template <typename IN_T, int CH>
+hipError_t launch_split(const BuildArgs& a, RowPlan pl, hipStream_t st) {
+  dim3 grid(a.batch * a.L * pl.S), block(256);
+  if (a.mode == 0) {
+    hipLaunchKernelGGL((k_rows<IN_T, 256, CH, false, true>), grid, block, 0, st, a, pl);
+    hipLaunchKernelGGL((k_rows_sum<IN_T, 256, CH, false>), grid, block, 0, st, a, pl);
+  } else {
+    hipLaunchKernelGGL((k_rows<IN_T, 256, CH, true, true>), grid, block, 0, st, a, pl);
+    hipLaunchKernelGGL((k_rows_sum<IN_T, 256, CH, true>), grid, block, 0, st, a, pl);
   }
   return hipGetLastError();
 }
 
 template <typename IN_T>
-hipError_t launch_dt(const BuildArgs& a, hipStream_t st) {
+hipError_t launch_dt(const BuildArgs& a, RowPlan pl, hipStream_t st) {
   constexpr int EPV = Elem<IN_T>::kPerVec;
-  const size_t esize = sizeof(IN_T);
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) &&
-                      ((size_t)a.V * esize) % 16 == 0;
-  if (!vec_ok) return launch_t<IN_T, 256, -1>(a, st);
+  if (pl.S > 1) {
+    const int ch = (pl.cv + 255) / 256;
+    if (ch <= 1) return launch_split<IN_T, 1>(a, pl, st);
+    if (ch <= 2) return launch_split<IN_T, 2>(a, pl, st);
+    if (ch <= 4) return launch_split<IN_T, 4>(a, pl, st);
+    return launch_split<IN_T, 8>(a, pl, st);
+  }
+  if (!pl.vec_ok) return launch_t<IN_T, 256, -1>(a, pl, st);
   const int nvec = a.V / EPV;
-  if (nvec <= 256) return launch_t<IN_T, 256, 1>(a, st);
+  if (nvec <= 256) return launch_t<IN_T, 256, 1>(a, pl, st);
   const int ch = (nvec + 511) / 512;
-  if (ch <= 4) return launch_t<IN_T, 512, 4>(a, st);
-  if (ch <= 8) return launch_t<IN_T, 512, 8>(a, st);
-  if (ch <= 16) return launch_t<IN_T, 512, 16>(a, st);
-  if (ch <= 40) return launch_t<IN_T, 512, 40>(a, st);
-  return launch_t<IN_T, 512, 0>(a, st);
+  if (ch <= 4) return launch_t<IN_T, 512, 4>(a, pl, st);
+  if (ch <= 8) return launch_t<IN_T, 512, 8>(a, pl, st);
+  if (ch <= 16) return launch_t<IN_T, 512, 16>(a, pl, st);
+  if (ch <= 40) return launch_t<IN_T, 512, 40>(a, pl, st);
+  return launch_t<IN_T, 512, 0>(a, pl, st);
 }
 
 }  // namespace
 
-size_t build_workspace_bytes(int batch, int L, int K) {
-  size_t n = (size_t)batch * L * K;
-  return align_up(n * 4, 256) * 2 + align_up((size_t)batch * L * 4, 256);
+// Rows are split when there are too few of them to give the chip ~512
+// workgroups: S chunks of cv >= 128 vectors each (so no chunk is empty),
+// S <= 32 and S * K <= 512 (the merge holds 8 words per lane).
+RowPlan plan_rows(int batch, int L, int V, int K, int esize, bool vec_ok) {
+  RowPlan pl{1, 0, vec_ok};
+  const int rows = batch * L;
+  const int nvec = (int)(((long long)V * esize) / 16);
+  if (!vec_ok || rows >= 256) return pl;
+  int S = std::min(32, 512 / K);
+  S = std::min(S, (512 + rows - 1) / rows);
+  S = std::min(S, nvec / 128);
+  if (S <= 1) return pl;
+  pl.S = S;
+  pl.cv = (nvec + S - 1) / S;
+  if (pl.cv > 8 * 256) pl.S = 1;  // chunk too long for the register-resident split kernels
+  return pl;
 }
 
-void build_carve(void* ws, int batch, int L, int K, int32_t** topk_tok, float** topk_lp,
-                 int32_t** row_flags) {
+size_t build_workspace_bytes(int batch, int L, int V, int K) {
+  // the largest plan over both element sizes (f32 rows have the most vectors)
+  const RowPlan p4 = plan_rows(batch, L, V, K, 4, true), p2 = plan_rows(batch, L, V, K, 2, true);
+  return build_layout(batch, L, K, std::max(p4.S, p2.S), nullptr, nullptr);
+}
+
+size_t build_layout(int batch, int L, int K, int S, void* ws, BuildArgs* a) {
+  const size_t rows = (size_t)batch * L;
   char* p = static_cast<char*>(ws);
-  size_t n = (size_t)batch * L * K;
-  *topk_tok = reinterpret_cast<int32_t*>(p);
-  p += align_up(n * 4, 256);
-  *topk_lp = reinterpret_cast<float*>(p);
-  p += align_up(n * 4, 256);
-  *row_flags = reinterpret_cast<int32_t*>(p);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += align_up(bytes, 256);
+    return q;
+  };
+  char* row_cand = take(rows * K * 8);
+  char* row_sum = take(rows * S * 8);
+  char* row_max = take(rows * 4);
+  char* row_flags = take(rows * 4);
+  char* part_cand = S > 1 ? take(rows * S * K * 8) : nullptr;
+  char* part_max = S > 1 ? take(rows * S * 4) : nullptr;
+  char* part_flags = S > 1 ? take(rows * S * 4) : nullptr;
+  if (a) {
+    a->row_cand = reinterpret_cast<uint64_t*>(row_cand);
+    a->row_sum = reinterpret_cast<uint64_t*>(row_sum);
+    a->row_max = reinterpret_cast<float*>(row_max);
+    a->row_flags = reinterpret_cast<int32_t*>(row_flags);
+    a->part_cand = reinterpret_cast<uint64_t*>(part_cand);
+    a->part_max = reinterpret_cast<float*>(part_max);
+    a->part_flags = reinterpret_cast<int32_t*>(part_flags);
+  }
+  return off;
 }
 
-
-hipError_t launch_build(const BuildArgs& a, hipStream_t st) {
-  hipError_t e = (a.dtype == 0) ? launch_dt<uint16_t>(a, st) : launch_dt<float>(a, st);
+hipError_t launch_build(BuildArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
+  const int esize = a.dtype == 0 ? 2 : 4;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) &&
+                      ((size_t)a.V * esize) % 16 == 0;
+  const RowPlan pl = plan_rows(a.batch, a.L, a.V, a.K, esize, vec_ok);
+  if (build_layout(a.batch, a.L, a.K, pl.S, nullptr, nullptr) > ws_bytes) return hipErrorInvalidValue;
+  build_layout(a.batch, a.L, a.K, pl.S, ws, &a);
+  hipError_t e = (a.dtype == 0) ? launch_dt<uint16_t>(a, pl, st) : launch_dt<float>(a, pl, st);
   if (e != hipSuccess) return e;
-  TreeArgs t{a.topk_tok, a.topk_lp, a.row_flags, a.root_tokens, a.L, a.K, a.N,
-             a.tokens, a.parents, a.depths, a.scores, a.num_nodes, a.mask, a.status};
+  TreeArgs t{};
+  t.row_cand = a.row_cand;
+  t.row_sum = a.row_sum;
+  t.row_max = a.row_max;
+  t.row_flags = a.row_flags;
+  t.S = pl.S;
+  t.mode = a.mode;
+  t.root_tokens = a.root_tokens;
+  t.L = a.L;
+  t.K = a.K;
+  t.N = a.N;
+  t.tokens = a.tokens;
+  t.parents = a.parents;
+  t.depths = a.depths;
+  t.scores = a.scores;
+  t.num_nodes = a.num_nodes;
+  t.mask = a.mask;
+  t.topk_tok = a.topk_tok;
+  t.topk_lp = a.topk_lp;
+  t.status = a.status;
   return launch_tree(t, a.batch, st);
 }
 

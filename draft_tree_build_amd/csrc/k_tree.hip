@@ -1,9 +1,12 @@
-// Best-first draft tree and its ancestor bitmask on gfx950 (k_tree).
+// Draft-tree log-probabilities, best-first tree and ancestor bitmask on
+// gfx950 (k_tree).
 //
 // Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees"
 // (Ringel, Romano), summary page, cited as [BDDT <section>].
 //
-// One workgroup per request. Wave 0 runs the N pops of the best-first
+// One workgroup per request. The workgroup first turns the row stage's
+// candidate words, maxima and fixed-point sums into the top-K tables
+// (token, log-probability) per position. Wave 0 then runs the N pops of the best-first
 // search [BDDT §4.3, App. A]. The best pending candidates are kept sorted
 // across the 64 lanes of the wave (lane j holds the j-th best), so a pop is
 // a read of lane 0, and the popped node's two successors are merged in with
@@ -37,6 +40,8 @@ struct TreeShared {
     uint64_t over[kOverCap];    // overflow candidates (during the pops)
     int32_t par[kMaxT];         // parents (mask walk, afterwards)
   };
+  float rmax[64];               // row maxima
+  float rlse[64];               // row log-normalisers
   int cmd;                      // 1: sort the overflow list; 0: pops finished
   int nover;
   int nn;
@@ -266,17 +271,48 @@ __global__ __launch_bounds__(kBlock) void k_tree(TreeArgs a) {
   __shared__ TreeShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
-  const int K = a.K;
-  const int LK = a.L * K;
+  const int K = a.K, L = a.L, S = a.S;
+  const int LK = L * K;
+  const size_t r0 = (size_t)b * L;  // first drafter row of this request
+  // Tables of the row stage [BDDT §3, §4.3]: candidate words (staged with
+  // the key in the lp slot and the id word in the tok slot), row maxima and
+  // the fixed-point partial sums of every row.
   for (int i = tid; i < LK; i += kBlock) {
-    sh.tok[i] = a.topk_tok[(size_t)b * LK + i];
-    sh.lp[i] = a.topk_lp[(size_t)b * LK + i];
+    const uint64_t wd = a.row_cand[r0 * K + i];
+    sh.tok[i] = (int32_t)(uint32_t)wd;
+    sh.lp[i] = __uint_as_float((uint32_t)(wd >> 32));
   }
+  for (int i = tid; i < L * S; i += kBlock) sh.over[i] = a.row_sum[r0 * S + i];
+  if (tid < L) sh.rmax[tid] = a.row_max[r0 + tid];
   if (wid == 1 && a.status) {  // L <= 64 row flags, one per lane, OR-reduced
-    int f = lane < a.L ? a.row_flags[(size_t)b * a.L + lane] : 0;
+    int f = lane < L ? a.row_flags[r0 + lane] : 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, 64);
     if (lane == 0) a.status[b] = f;
+  }
+  __syncthreads();
+  if (tid < L) {  // log of the row's normaliser
+    uint64_t sum = 0;
+    for (int j = 0; j < S; ++j) sum += sh.over[tid * S + j];
+    sh.rlse[tid] = sh.rmax[tid] == -INFINITY ? INFINITY : lse_from_fixed(sum);
+  }
+  __syncthreads();
+  // log-probabilities: lp = (x - m) - lse, or at temperature 0 the argmax
+  // limit (0 - lse for the maximum, -inf elsewhere)
+  for (int i = tid; i < LK; i += kBlock) {
+    const int row = i / K;
+    const float x = order_to_float(__float_as_uint(sh.lp[i]));
+    const int id = (int)(0xFFFFFFFFu - (uint32_t)sh.tok[i]);
+    const float m = sh.rmax[row];
+    float lp = -INFINITY;
+    if (m != -INFINITY) {
+      const float d = (a.mode == 2) ? ((x == m) ? 0.0f : -INFINITY) : (x - m);
+      lp = d - sh.rlse[row];
+    }
+    sh.tok[i] = id;
+    sh.lp[i] = lp;
+    if (a.topk_tok) a.topk_tok[r0 * K + i] = id;
+    if (a.topk_lp) a.topk_lp[r0 * K + i] = lp;
   }
   __syncthreads();
   if (wid == 0) {

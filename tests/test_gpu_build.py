@@ -185,3 +185,18 @@ def test_build_overflow_refills(L, K, spread):
     note("build overflow L=%d K=%d spread=%g" % (L, K, spread))
     g, _ = gpu_build(x, [5, 6], K, N, 1.0)
     assert_same_build(g, o)
+
+
+@pytest.mark.parametrize("B,L,V,K", [(1, 2, 151936, 16), (16, 16, 5000, 8)])
+def test_build_all_equal_rows_exact_fallback(B, L, V, K):
+    """Rows of one repeated value: more tied candidates than the candidate
+    buffer holds, so the exact selection runs -- inside row chunks (few rows,
+    long vocabulary) and on whole rows (many rows)."""
+    x = torch.full((B, L, V), 0.25, dtype=torch.bfloat16)
+    x[0, 0, V // 3] = 1.0                          # one row with a single clear winner
+    roots = list(range(B))
+    for tau in (1.0, 0.0):
+        note("build all-equal B=%d L=%d V=%d K=%d tau=%g" % (B, L, V, K, tau))
+        g, _ = gpu_build(x, roots, K, 40, tau)
+        o = oracle.build_tree(x, roots, K, 40, tau)
+        assert_same_build(g, o)
