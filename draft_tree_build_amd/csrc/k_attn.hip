@@ -11,8 +11,10 @@
 // bf16, D = 128 (k_attn_mfma): one workgroup = 4 waves = 128 query rows of
 // one (request, kv-head) -- rows are node-major, the g = Hq/Hkv query heads
 // of a node adjacent, so GQA shares every K/V tile across g heads. Key tiles
-// of 64 rows are staged through LDS (K row-major, V transposed, both XOR
-// swizzled). Per wave and tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
+// of 64 rows go from HBM straight into LDS by DMA (global_load_lds, no
+// registers), row-major with an XOR swizzle of the 16-byte chunks; V
+// fragments come out transposed through ds_read_b64_tr_b16. Per wave and
+// tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
 // (lane = query row), online softmax in fp32 (exp2 domain), O^T += V^T P^T
 // with P split into two bf16 parts (hi + lo) so the weights stay ~fp32 exact.
 // The key tile list is prefix tiles then tree tiles (mask applied); long
@@ -35,22 +37,18 @@ constexpr int kTileRows = kRowsPerWave * kWavesA;  // 128
 constexpr int kKeys = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// K tile: 64 rows of 256 bytes (128 dims), row r at byte r*272 + (r/8)*64.
-// The padding puts the 8 lanes of a 128-bit fragment read -- keys
-// {0..3, 8..11} + c or {4..7, 12..15} + c -- on 8 distinct 16-byte bank
-// groups, and every fragment offset of a lane is a compile-time immediate.
-constexpr int kKRow = kD * 2 + 16;
-constexpr int kKBytes = (kKeys - 1) * kKRow + (kKeys / 8 - 1) * 64 + kD * 2;
-__device__ __forceinline__ int k_row_off(int key) { return key * kKRow + (key >> 3) * 64; }
-// V^T tile: [128 dims][8 chunks of 8 keys] = 128 bytes per dim, chunk index
-// XOR-swizzled by sw(dim) = (dim ^ (dim >> 3)) & 7. Fragment reads (32
-// consecutive dims) and transposed writes (dims 8 apart) both spread over
-// the banks; for dim = 32 db + n, sw = ((n ^ (n >> 3)) & 7) ^ 4 (db & 1).
-constexpr int kVBytes = kKeys * kD * 2;
-__device__ __forceinline__ int v_lds_off(int dim, int chunk) {
-  int sw = (dim ^ (dim >> 3)) & 7;
-  return dim * (kKeys * 2) + ((chunk ^ sw) << 4);
-}
+// K and V tiles: 64 rows of 256 bytes (128 dims) at row * 256; the 16-byte
+// chunk c of row r sits at physical chunk c ^ sw(r). sw takes 16 distinct
+// values over any 16 rows {0..3, 8..11} + 4j or 4 consecutive rows with
+// distinct bits 1..2, which keeps both the K fragment reads (16 keys, one
+// chunk each) and the V transpose reads (4 consecutive keys, 2 chunks each)
+// free of bank conflicts.
+constexpr int kTileBytes = kKeys * kD * 2;  // 16 KB
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short short8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
 
 struct AttnSplit {
   int nsplit;
@@ -69,8 +67,11 @@ constexpr int kXcds = 8;
 // LDS: tile t+1 is fetched into registers while tile t is computed.
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, float* part_o,
                                                       float* part_ml) {
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kKBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][kVBytes];
+  // two buffers of K and V tiles; 64 KB
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wi = (int)(blockIdx.x % kXcds) * pl.per_xcd + (int)(blockIdx.x / kXcds);
   if (wi >= pl.total) return;
@@ -138,11 +139,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // staging of one K/V tile: lane covers dim chunk dc and keys
-  // k0, k0+1, k0+8, k0+9 with k0 = 16 w + 2 kq
-  const int dc = lane & 15, kq = lane >> 4;
-  const int k0 = 16 * w + 2 * kq;
-  uint4 sk[4], sv[4];
+  // ---- staging by DMA: wave w moves rows 16 w .. 16 w + 15 of K and V, four
+  // 1 KB blocks each; lane i of a block writes LDS bytes 16 i of it, so it
+  // fetches row 4 blk + i / 16, logical chunk (i % 16) ^ sw(row).
+  const uint32_t row_bytes = (uint32_t)a.Hkv * kD * 2;
+  uint32_t dma_off[4];   // byte offset from the tile's first K/V row
+  int dma_row[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int blk = 4 * w + j;
+    const int r = 4 * blk + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    dma_row[j] = r;
+    dma_off[j] = (uint32_t)r * row_bytes + (uint32_t)hk * (kD * 2) + (uint32_t)c * 16;
+  }
   auto tile_rows = [&](int t, int* base, int* nvalid) __attribute__((always_inline)) {
     if (t < np) {
       *base = t * kKeys;
@@ -153,121 +163,101 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       *nvalid = min(kKeys, nn - tt * kKeys);
     }
   };
-  // per-lane element offsets inside a tile (32-bit); the tile base is uniform
-  const uint32_t row_elems = (uint32_t)a.Hkv * kD;
-  const uint32_t lane_off0 = (uint32_t)k0 * row_elems + hk * kD + 8 * dc;
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
+  auto dma_tile = [&](int t, unsigned char* kbuf, unsigned char* vbuf) __attribute__((always_inline)) {
     int base, nvalid;
     tile_rows(t, &base, &nvalid);
     const int64_t r0 = (int64_t)kv0 + base;  // first key row of the tile
-    const int64_t lim = min((int64_t)nvalid, a.total_rows - r0);
-    const size_t tb = (r0 < a.total_rows) ? (size_t)r0 * row_elems : 0;
-    const uint16_t* kt = Kg + tb;
-    const uint16_t* vt = Vg + tb;
+    const bool in_range = r0 < a.total_rows;
+    const int lim = in_range ? (int)min((int64_t)nvalid, a.total_rows - r0) : 0;
+    const size_t tb = in_range ? (size_t)r0 * row_bytes : 0;
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(Kg) + tb;
+    const unsigned char* vt = reinterpret_cast<const unsigned char*>(Vg) + tb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int jk = (j & 1) + 8 * (j >> 1);
-      const bool ok = (int64_t)(k0 + jk) < lim;
-      // out-of-range keys read the tile's first row (or row 0) and are zeroed
-      const uint32_t off = ok ? lane_off0 + (uint32_t)jk * row_elems : (uint32_t)(hk * kD + 8 * dc);
-      const uint4 kx = *reinterpret_cast<const uint4*>(kt + off);
-      const uint4 vx = *reinterpret_cast<const uint4*>(vt + off);
-      sk[j] = ok ? kx : make_uint4(0, 0, 0, 0);
-      sv[j] = ok ? vx : make_uint4(0, 0, 0, 0);
-    }
-  };
-  // K: 128-bit writes; V: transposed 32-bit writes of key pairs
-  auto write_tile = [&](int bf) __attribute__((always_inline)) {
-    unsigned char* kl = k_lds[bf];
-    unsigned char* vl = v_lds[bf];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + (j & 1) + 8 * (j >> 1);
-      *reinterpret_cast<uint4*>(kl + k_row_off(key) + 16 * dc) = sk[j];
-    }
-#pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-      const uint4 va = sv[2 * hp], vb = sv[2 * hp + 1];
-      const int key = k0 + 8 * hp;  // even; key+1 in the same 8-key chunk
-      const uint32_t aw[4] = {va.x, va.y, va.z, va.w};
-      const uint32_t bw[4] = {vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (e & 1) ? (aw[e >> 1] >> 16) : (aw[e >> 1] & 0xFFFFu);
-        const uint32_t hi = (e & 1) ? (bw[e >> 1] & 0xFFFF0000u) : (bw[e >> 1] << 16);
-        const int dim = 8 * dc + e;
-        *reinterpret_cast<uint32_t*>(vl + v_lds_off(dim, key >> 3) + (key & 7) * 2) = lo | hi;
-      }
+      // rows past the tile's end re-read the tile's first row: their scores
+      // are masked, so they only ever meet zero weights
+      const uint32_t off = dma_row[j] < lim ? dma_off[j] : dma_off[j] - (uint32_t)dma_row[j] * row_bytes;
+      unsigned char* kd = kbuf + (4 * w + j) * 1024;
+      unsigned char* vd = vbuf + (4 * w + j) * 1024;
+      __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt + off, (__attribute__((address_space(3))) void*)vd, 16, 0, 0);
     }
   };
 
-  // the key permutation of the S^T A operand: A row m -> key pi(m), chosen so
-  // that lane group gq's score registers v = 0..7 hold keys 8 gq + v and
-  // v = 8..15 hold keys 16 + 8 gq + (v - 8) of each 32-key block
+  // ---- fragment addresses (bytes within a tile)
+  // K (A operand of S^T): lane row m -> key pi(m), chosen so that lane group
+  // gq's score registers v = 0..7 hold keys 8 gq + v and v = 8..15 hold keys
+  // 16 + 8 gq + (v - 8) of each 32-key half; dims 16 ks + 8 gq + 0..7.
   const int m_a = lane & 31;
   const int pi_m = 8 * ((m_a >> 2) & 1) + 16 * (m_a >> 4) + 4 * ((m_a >> 3) & 1) + (m_a & 3);
-  const int kfrag0 = k_row_off(pi_m) + 16 * gq;  // + 32 ks, + kb block offset
-  // V^T fragment addresses for dims 32 db + n: the 4 chunk offsets of this
-  // lane; odd db flips swizzle bit 2, each db adds 32 dims * 128 bytes
-  int vfrag[4];
-  {
-    const int sw = (n ^ (n >> 3)) & 7;
+  int kfrag[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int chunk = 4 * (c >> 1) + 2 * (c & 1) + gq;  // kb = c/2, hf = c%2
-      vfrag[c] = n * (kKeys * 2) + ((chunk ^ sw) << 4);
+  for (int ks = 0; ks < 8; ++ks) kfrag[ks] = tile_off(pi_m, 2 * ks + gq);
+  // V (A operand of O^T = V^T P^T, read transposed): 16-lane group G holds
+  // dims 32 db + 16 (G % 2) + t and keys 16 hf + 8 (G / 2) + 0..7 of a half;
+  // transpose-read rd covers keys + 4 rd .. + 3, lane i of the group pointing
+  // at row + i / 4, dims + 4 (i % 4) .. + 3.
+  const int G = lane >> 4, ti = lane & 15;
+  int vfrag[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int row = 8 * (G >> 1) + 4 * rd + (ti >> 2);     // + 32 kb + 16 hf (keep sw)
+      const int dim = 32 * db + 16 * (G & 1) + 4 * (ti & 3);
+      vfrag[db][rd] = tile_off(row, dim >> 3) + ((dim & 7) << 1);
     }
-  }
 
   // mask word of this lane's query row for tree tile t (prefetched with the tile)
   const uint64_t* mrow = a.mask + ((size_t)b * T + node) * W;
   auto load_mword = [&](int t) __attribute__((always_inline)) -> uint64_t {
     return (t >= np && row_valid) ? mrow[t - np] : 0ull;
   };
-  int bf = 0;
-  uint64_t mword_next = 0;
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    mword_next = load_mword(t_begin);
-    write_tile(0);
-  }
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const bool has_next = t + 1 < t_end;
-    const uint64_t mword = mword_next;
-    if (has_next) {  // in flight while tile t is computed
-      load_tile(t + 1);
-      mword_next = load_mword(t + 1);
-    }
-    const unsigned char* kl = k_lds[bf];
-    const unsigned char* vl = v_lds[bf];
-
+  // One key tile from LDS (kl, vl: the tile's K and V buffers).
+  auto tile_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl)
+      __attribute__((always_inline)) {
     int base, nvalid;
     tile_rows(t, &base, &nvalid);
     const bool tree_tile = t >= np;
+    const bool need_mask = tree_tile || nvalid < kKeys;
+    // allowed keys of this lane's query row: in range and (tree tiles) ancestors
+    uint64_t allow = nvalid >= kKeys ? ~0ull : ((1ull << nvalid) - 1ull);
+    if (tree_tile) allow &= mword;
 
     // ---- two halves of 32 keys: S^T = K Q^T, online softmax, O^T += V^T P^T
-    const bool need_mask = tree_tile || nvalid < kKeys;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kf[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + kb * 32 * 256);
       floatx16 sc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + kfrag0 + kb * (32 * kKRow + 4 * 64) + 32 * ks);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc, 0, 0, 0);
-      }
+      for (int ks = 0; ks < 8; ++ks) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
+      // V fragments of this half, read while the scores are computed
+      bf16x8 vf[4][2];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int kofs = (32 * kb + 16 * hf) * 256;
+          const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][0] + kofs));
+          const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][1] + kofs));
+          vf[db][hf] = __builtin_bit_cast(bf16x8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        }
       // mask (tree tiles and the ragged last prefix tile only) and row max.
       // Query rows past num_nodes need no masking: their scores never reach
       // a valid row and their outputs are written as zeros.
       float tmax = -INFINITY;
       if (need_mask) {
+        // register v holds key 32 kb + 8 gq + v (v < 8) or + 8 more (v >= 8)
+        const uint32_t sh = 32 * kb + 8 * gq;
+        const uint32_t bits = (uint32_t)((allow >> sh) & 0xFFull) | ((uint32_t)((allow >> (sh + 16)) & 0xFFull) << 8);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int kk = 32 * kb + 8 * gq + (v < 8 ? v : v + 8);
-          const bool ok = kk < nvalid && (!tree_tile || ((mword >> kk) & 1ull) != 0);
-          sc[v] = ok ? sc[v] : -INFINITY;
+          sc[v] = ((bits >> v) & 1u) ? sc[v] : -INFINITY;
           tmax = fmaxf(tmax, sc[v]);
         }
       } else {
@@ -312,19 +302,46 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       }
       m_run = m_new;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int va = ((db & 1) ? (vfrag[2 * kb + hf] ^ 64) : vfrag[2 * kb + hf]) + db * 32 * kKeys * 2;
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + va);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[hf], acc_o[db], 0, 0, 0);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[hf], acc_o[db], 0, 0, 0);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][hf], pf[hf], acc_o[db], 0, 0, 0);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][hf], pl[hf], acc_o[db], 0, 0, 0);
         }
-      }
     }
-    if (has_next) write_tile(bf ^ 1);
-    __syncthreads();
-    bf ^= 1;
+  };
+
+  // Tiles alternate between two LDS buffers (static, so that the compiler
+  // sees the DMA into one buffer and the reads of the other as disjoint):
+  // while tile t is computed from one buffer, tile t+1 lands in the other.
+  uint64_t mword_next = 0;
+  if (t_begin < t_end) {
+    dma_tile(t_begin, k_lds0, v_lds0);
+    mword_next = load_mword(t_begin);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = t_begin; t < t_end; t += 2) {
+    {
+      const uint64_t mword = mword_next;
+      if (t + 1 < t_end) {
+        dma_tile(t + 1, k_lds1, v_lds1);
+        mword_next = load_mword(t + 1);
+      }
+      tile_body(t, mword, k_lds0, v_lds0);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
+      __syncthreads();
+    }
+    if (t + 1 < t_end) {
+      const uint64_t mword = mword_next;
+      if (t + 2 < t_end) {
+        dma_tile(t + 2, k_lds0, v_lds0);
+        mword_next = load_mword(t + 2);
+      }
+      tile_body(t + 1, mword, k_lds1, v_lds1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   const float l_row = l_run + __shfl_xor(l_run, 32, 64);
