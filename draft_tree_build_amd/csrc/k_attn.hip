@@ -38,16 +38,16 @@ constexpr int kKeys = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // K and V tiles: 64 rows of 256 bytes (128 dims) at row * 256; the 16-byte
-// chunk c of row r sits at physical chunk c ^ sw(r). sw takes 16 distinct
-// values over any 16 rows {0..3, 8..11} + 4j or 4 consecutive rows with
-// distinct bits 1..2, which keeps both the K fragment reads (16 keys, one
+// chunk c of row r sits at physical chunk c ^ sw(r), sw(r) = the low four
+// row bits with their two pairs swapped. Measured on gfx950 (LDS bank
+// conflict counter), this keeps both the K fragment reads (16 keys, one
 // chunk each) and the V transpose reads (4 consecutive keys, 2 chunks each)
 // free of bank conflicts.
 constexpr int kTileBytes = kKeys * kD * 2;  // 16 KB
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short short8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
 
 struct AttnSplit {

@@ -54,6 +54,7 @@ SMALL = [
     (2, 2, 20, 2, 20, 8, 1, [200, 7]),          # budget above the restricted set: padding rows
     (1, 16, 80, 8, 64, 32, 8, [2048]),          # split-KV path
     (1, 5, 60, 6, 200, 64, 8, [900]),           # g = 8, many row tiles
+    (2, 6, 60, 6, 300, 32, 8, [3000, 1500]),    # split, many row tiles, ragged last row tile
 ]
 
 
