@@ -34,12 +34,13 @@ DEFAULT_WORKLOAD = "L16_V32000_K8_N64_P2048"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 KERNEL_SOURCES = {
-    "build": "draft_tree_build_amd/csrc/k_build.hip",
-    "verify": "draft_tree_build_amd/csrc/k_attn.hip",
-    "accept": "draft_tree_build_amd/csrc/k_accept.hip",
+    "build": ["draft_tree_build_amd/csrc/k_build.hip", "draft_tree_build_amd/csrc/k_tree.hip"],
+    "verify": ["draft_tree_build_amd/csrc/k_attn.hip"],
+    "accept": ["draft_tree_build_amd/csrc/k_accept.hip"],
 }
-KERNEL_NAMES = {"build": "k_rows+k_tree", "verify": "k_attn_mfma(+k_attn_combine)",
-                "accept": "k_argmax+k_walk"}
+KERNEL_NAMES = {"build": "ddtree_build: k_rows (+ k_rows_sum for split rows), k_tree",
+                "verify": "ddtree_verify_attn: k_attn_mfma (+ k_attn_combine for split keys)",
+                "accept": "ddtree_accept: k_argmax, k_walk"}
 
 
 def log(msg):
@@ -63,9 +64,12 @@ def algorithmic_work(w, prefix_lens, num_nodes, depths, esize):
                 accept_bytes=accept_bytes)
 
 
-def source_hash(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload, stage):
@@ -175,19 +179,20 @@ def main():
     num_nodes = rnd.num_nodes.cpu()
     nodes_per_step = int((num_nodes - 1).sum())
 
-    # Per input copy, one HIP graph holding the whole round and one graph per
-    # stage. Most timed steps replay the whole-round graph (no host launch
-    # overhead between the ABI calls). Every SAMPLE_EVERY-th step replays the
-    # stage graphs instead, with HIP events between them on the same stream:
-    # those events time each stage inside the timed region. --no-graphs
-    # launches the calls eagerly, every step with events.
+    # Per input copy, one HIP graph holding the whole round. Most timed steps
+    # replay it (no host launch overhead between the ABI calls). Every
+    # SAMPLE_EVERY-th step calls the three ABI functions directly instead,
+    # with HIP events between them on the same stream: those events time each
+    # stage inside the timed region (the graph replays queued ahead keep the
+    # GPU from waiting on the host there). --no-graphs launches every step
+    # directly, with events.
     SAMPLE_EVERY = 20
-    whole, per_stage = None, None
+    whole = None
     if args.graphs:
-        log("capturing %d x 4 graphs" % R)
+        log("capturing %d graphs" % R)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        whole, per_stage = [], []
+        whole = []
         with torch.cuda.stream(side):
             for c in range(R):
                 g = torch.cuda.CUDAGraph()
@@ -195,18 +200,9 @@ def main():
                     for f in stages:
                         f(copies[c])
                 whole.append(g)
-                row = []
-                for f in stages:
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=side):
-                        f(copies[c])
-                    row.append(g)
-                per_stage.append(row)
         torch.cuda.current_stream().wait_stream(side)
         for i in range(min(R, args.warmup)):
             whole[i].replay()
-            for g in per_stage[i]:
-                g.replay()
         torch.cuda.synchronize()
 
     sampled = [i for i in range(args.steps)
@@ -223,10 +219,7 @@ def main():
             continue
         ev[0].record()
         for k in range(3):
-            if per_stage is not None:
-                per_stage[c][k].replay()
-            else:
-                stages[k](copies[c])
+            stages[k](copies[c])
             ev[k + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
