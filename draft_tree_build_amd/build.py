@@ -26,8 +26,15 @@ FLAGS = [
 ]
 
 
+# The row kernels keep a whole row in registers and visit it in fully
+# unrolled loops; their bodies exceed LLVM's default size limit for a forced
+# unroll, and a loop left rolled would index the register copy dynamically
+# (moving it to scratch memory).
+EXTRA = {"k_build.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

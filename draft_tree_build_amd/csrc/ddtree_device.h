@@ -52,13 +52,17 @@ __device__ __forceinline__ double exp_fixed(float d) {
   t = fmaxf(t, -64.0f);
   float n = rintf(t);
   float f = t - n;
-  float p = 0x1.5d87fep-10f;            // (ln2)^5/120
-  p = fmaf(p, f, 0x1.3b2ab6p-7f);       // (ln2)^4/24
-  p = fmaf(p, f, 0x1.c6b08ep-5f);       // (ln2)^3/6
-  p = fmaf(p, f, 0x1.ebfbe0p-3f);       // (ln2)^2/2
-  p = fmaf(p, f, 0x1.62e430p-1f);       // ln2
-  p = fmaf(p, f, 1.0f);
-  float e = ldexpf(p, (int)n + 44);
+  // The Horner steps run on the coefficients times 2^44: each step is then
+  // exactly 2^44 times the unscaled one (scaling by a power of two commutes
+  // with rounding while every value stays normal), which saves the + 44 on
+  // the exponent.
+  float p = 0x1.5d87fep+34f;            // (ln2)^5/120 * 2^44
+  p = fmaf(p, f, 0x1.3b2ab6p+37f);      // (ln2)^4/24 * 2^44
+  p = fmaf(p, f, 0x1.c6b08ep+39f);      // (ln2)^3/6 * 2^44
+  p = fmaf(p, f, 0x1.ebfbe0p+41f);      // (ln2)^2/2 * 2^44
+  p = fmaf(p, f, 0x1.62e430p+43f);      // ln2 * 2^44
+  p = fmaf(p, f, 0x1p+44f);             // 1 * 2^44
+  float e = ldexpf(p, (int)n);
   return (double)rintf(e);
 }
 
@@ -124,6 +128,77 @@ __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
+}
+
+// Wave reductions through DPP row operations (no LDS round trip, unlike the
+// shuffles above): lane ^ 1, lane ^ 2, the other quad of each 8, the other 8
+// of each 16, then row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3).
+// Lane 63 then holds the reduction over all 64 lanes; v_readlane returns it
+// to every lane. Rows not written by a step keep `identity`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_src(uint32_t identity, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <class F>
+__device__ __forceinline__ uint32_t dpp_reduce(uint32_t v, uint32_t identity, F op) {
+  v = op(v, dpp_src<0xB1, 0xF>(identity, v));
+  v = op(v, dpp_src<0x4E, 0xF>(identity, v));
+  v = op(v, dpp_src<0x141, 0xF>(identity, v));
+  v = op(v, dpp_src<0x140, 0xF>(identity, v));
+  v = op(v, dpp_src<0x142, 0xA>(identity, v));
+  v = op(v, dpp_src<0x143, 0xC>(identity, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_src64(uint64_t identity, uint64_t v) {
+  const uint32_t lo = dpp_src<CTRL, ROW_MASK>((uint32_t)identity, (uint32_t)v);
+  const uint32_t hi = dpp_src<CTRL, ROW_MASK>((uint32_t)(identity >> 32), (uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <class F>
+__device__ __forceinline__ uint64_t dpp_reduce64(uint64_t v, uint64_t identity, F op) {
+  v = op(v, dpp_src64<0xB1, 0xF>(identity, v));
+  v = op(v, dpp_src64<0x4E, 0xF>(identity, v));
+  v = op(v, dpp_src64<0x141, 0xF>(identity, v));
+  v = op(v, dpp_src64<0x140, 0xF>(identity, v));
+  v = op(v, dpp_src64<0x142, 0xA>(identity, v));
+  v = op(v, dpp_src64<0x143, 0xC>(identity, v));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  return __uint_as_float(dpp_reduce(__float_as_uint(v), __float_as_uint(-INFINITY), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  return dpp_reduce(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_or_dpp(uint32_t v) {
+  return dpp_reduce(v, 0u, [](uint32_t a, uint32_t b) { return a | b; });
+}
+__device__ __forceinline__ uint64_t wave_sum_u64_dpp(uint64_t v) {
+  return dpp_reduce64(v, 0ull, [](uint64_t a, uint64_t b) { return a + b; });
+}
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  return dpp_reduce64(v, 0ull, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+}
+
+// The k-th largest (k >= 1) of the 64 lanes' values, by a radix select on
+// ballots, two bits per step: the largest t with at least k lanes holding
+// >= t. Returns 0 when k > 64.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int sh = 30; sh >= 0; sh -= 2) {
+    const uint32_t c1 = t | (1u << sh), c2 = t | (2u << sh), c3 = t | (3u << sh);
+    const int n1 = __popcll(__ballot(v >= c1));
+    const int n2 = __popcll(__ballot(v >= c2));
+    const int n3 = __popcll(__ballot(v >= c3));
+    t = n3 >= k ? c3 : (n2 >= k ? c2 : (n1 >= k ? c1 : t));
+  }
+  return t;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

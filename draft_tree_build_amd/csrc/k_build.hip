@@ -24,7 +24,6 @@ constexpr int kMaxT = 1025;
 
 struct RowShared {
   uint64_t cand[kCandMax];
-  uint32_t gmax[64];
 };
 
 // ------------------------------------------------------------------ input views
@@ -212,6 +211,21 @@ __device__ void bitonic_desc(uint64_t* s, int P) {
   }
 }
 
+// Number of words in s[0..n) (LDS, n >= 1) greater than w. Sixteen reads
+// are issued before the first compare so that LDS latency is paid once per
+// sixteen words; indexes past the end re-read s[n-1] and are not counted.
+__device__ __forceinline__ int count_greater(const uint64_t* s, int n, uint64_t w) {
+  int c = 0;
+  for (int j = 0; j < n; j += 16) {
+    uint64_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = s[min(j + u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c += (j + u < n && v[u] > w) ? 1 : 0;
+  }
+  return c;
+}
+
 // Candidate word for the top-K sort: larger = better = (x desc, id asc).
 __device__ __forceinline__ uint64_t cand_word(uint32_t key, int id) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
@@ -225,12 +239,14 @@ __device__ __forceinline__ uint64_t cand_word(uint32_t key, int id) {
 // adds the chunk sums and merges the chunk candidates.
 template <typename IN_T, int BLOCK, int CH, bool GENERAL, bool PART>
 __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a, RowPlan pl) {
+  constexpr int NW = BLOCK / 64;
   __shared__ RowShared sm_row;
-  __shared__ float red_f[16];
+  __shared__ float red_f[NW];
   __shared__ int red_i[16];
-  __shared__ uint64_t red_u[16];
+  __shared__ uint32_t red_t[NW];
+  __shared__ uint64_t red_u[NW];
+  __shared__ int red_c[NW];
   __shared__ int s_cnt;
-  __shared__ uint32_t s_t0;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = PART ? (int)blockIdx.x / pl.S : (int)blockIdx.x;
@@ -266,131 +282,207 @@ __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a, RowPlan pl) {
   bool has = false;
   view.visit(tid, [&](int, float raw) __attribute__((always_inline)) {
     float x = xval(raw);
-    bool bad = (x != x) || (x == INFINITY);
+    const bool bad = __builtin_amdgcn_classf(x, 0x203);  // NaN or +inf
     tflag |= bad ? 1 : 0;
     x = bad ? -INFINITY : x;
     tmax = fmaxf(tmax, x);
     has = true;
   });
-  const float m = block_max<BLOCK>(tmax, red_f);
-  int flags = block_or<BLOCK>(tflag, red_i);
 
-  // ---- a lower bound t0 for the K-th largest key: the K-th largest of 64
-  //      group maxima (each is a distinct element of the row)
-  uint32_t tkey = has ? float_order(tmax) : 0u;
-  constexpr int G = BLOCK / 64;
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) {
-    uint32_t w = __shfl_xor(tkey, o, 64);
-    tkey = w > tkey ? w : tkey;
-  }
-  if ((tid % G) == 0) sm_row.gmax[tid / G] = tkey;
-  if (tid == 0) s_cnt = 0;
-  __syncthreads();
-  if (wid == 0) {
-    uint32_t v = sm_row.gmax[lane];
-    for (int k = 2; k <= 64; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        uint32_t o = __shfl_xor(v, j, 64);
-        bool desc = (lane & k) == 0;
-        bool low = (lane & j) == 0;
-        v = (low == desc) ? (o > v ? o : v) : (o < v ? o : v);
-      }
+  // ---- per wave: maximum, status bits, and the K-th largest of its lanes'
+  //      maxima (each a distinct element of the row); the largest of the
+  //      waves' K-th values is a lower bound t0 for the row's K-th largest key
+  {
+    const float wm = wave_max_dpp(tmax);
+    const uint32_t wf = wave_or_dpp((uint32_t)tflag);
+    const uint32_t wt = wave_kth_largest(has ? float_order(tmax) : 0u, K);
+    if (lane == 0) {
+      red_f[wid] = wm;
+      red_i[wid] = (int)wf;
+      red_t[wid] = wt;
     }
-    uint32_t t0 = __shfl(v, K - 1, 64);
-    if (lane == 0) s_t0 = t0;
   }
   __syncthreads();
-  const uint32_t t0 = s_t0;
+  float m = red_f[0];
+  int flags = red_i[0];
+  uint32_t t0 = red_t[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    m = fmaxf(m, red_f[w]);
+    flags |= red_i[w];
+    t0 = max(t0, red_t[w]);
+  }
+  // every element with key >= t0 compares >= t0f (a superset when t0f is
+  // +0, which also admits -0: harmless, the sort below uses exact keys)
+  const float t0f = t0 == 0u ? -INFINITY : order_to_float(t0);
 
   auto key_of = [&](float raw) __attribute__((always_inline)) -> uint32_t {
     float x = xval(raw);
     x = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
     return float_order(x);
   };
+  // candidates go to the wave's own segment of the buffer, at positions
+  // from the ballot (no atomics); wcnt is the wave's running count
+  constexpr int SEG = kCandMax / NW;
+  uint64_t* const seg = sm_row.cand + wid * SEG;
+  int wcnt = 0;
+  auto take = [&](int id, float xs) __attribute__((always_inline)) {
+    const bool hit = xs >= t0f;
+    const uint64_t bal = __ballot(hit);
+    if (bal != 0ull) {
+      const int pos = wcnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (hit && pos < SEG) seg[pos] = cand_word(float_order(xs), id);
+      wcnt += __popcll(bal);
+    }
+  };
 
-  // ---- pass 2: candidates (every element with key >= t0); without a split
-  //      also the exact fixed-point normaliser S = sum_v rint(2^44 E(x_v - m))
+  // ---- pass 2: candidates; without a split also the exact fixed-point
+  //      normaliser S = sum_v rint(2^44 E(x_v - m))
   double acc = 0.0;
   const bool finite_m = m != -INFINITY;
   view.fence();
-  view.visit(tid, [&](int id, float raw) __attribute__((always_inline)) {
-    const float x = xval(raw);
-    const float xs = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
-    const uint32_t kk = float_order(xs);
-    if (kk >= t0) {
-      const int c = atomicAdd(&s_cnt, 1);
-      if (c < kCandMax) sm_row.cand[c] = cand_word(kk, id);
-    }
-    if (!PART) {
-      float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
-      d = finite_m ? d : -INFINITY;
-      acc += exp_fixed(d);
-    }
-  });
-  __syncthreads();
-  const int ncand = s_cnt;
-  int nsort;
-  if (ncand <= kCandMax) {
-    nsort = ncand;
-  } else {
-    // Exact fallback (rows with very many near-top ties): find the K-th
-    // largest key bit by bit, then keep the keys above it and the lowest ids
-    // among the keys equal to it.
-    uint32_t t = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = t | (1u << bit);
-      int cnt = 0;
-      view.visit_mem(tid, [&](int, float raw) __attribute__((always_inline)) { cnt += key_of(raw) >= c ? 1 : 0; });
-      if (block_sum<BLOCK>(cnt, red_i) >= K) t = c;
-    }
-    int gt = 0;
-    view.visit_mem(tid, [&](int, float raw) __attribute__((always_inline)) { gt += key_of(raw) > t ? 1 : 0; });
-    const int ngt = block_sum<BLOCK>(gt, red_i);
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    view.visit_mem(tid, [&](int id, float raw) __attribute__((always_inline)) {
-      uint32_t kk = key_of(raw);
-      if (kk > t) sm_row.cand[atomicAdd(&s_cnt, 1)] = cand_word(kk, id);
+  if (flags == 0 && finite_m && !(GENERAL && mode == 2)) {
+    // no NaN or +inf in the row: values need no sanitising
+    view.visit(tid, [&](int id, float raw) __attribute__((always_inline)) {
+      const float x = xval(raw);
+      take(id, x);
+      if (!PART) acc += exp_fixed(x - m);
     });
-    const int need = K - ngt;
-    int base = 0;
-    const int nc = view.num_chunks();
-    for (int c = 0; c < nc && base < need; ++c) {
-      int local = 0;
-      view.visit_chunk(c, tid, [&](int, float raw) __attribute__((always_inline)) { local += key_of(raw) == t ? 1 : 0; });
-      int excl;
-      const int total = block_exclusive_scan<BLOCK>(local, &excl, red_i);
-      int j = 0;
-      view.visit_chunk(c, tid, [&](int id, float raw) __attribute__((always_inline)) {
-        if (key_of(raw) == t) {
-          if (base + excl + j < need) sm_row.cand[atomicAdd(&s_cnt, 1)] = cand_word(t, id);
-          ++j;
-        }
-      });
-      base += total;
+  } else {
+    // (rows with NaN / +inf, argmax mode): on long rows this pass re-reads
+    // memory, so that the register copy is visited by one unrolled loop only
+    auto general = [&](int id, float raw) __attribute__((always_inline)) {
+      const float x = xval(raw);
+      const float xs = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
+      take(id, xs);
+      if (!PART) {
+        float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
+        d = finite_m ? d : -INFINITY;
+        acc += exp_fixed(d);
+      }
+    };
+    if constexpr (CH > 8) {
+      view.visit_mem(tid, general);
+    } else {
+      view.visit(tid, general);
     }
-    __syncthreads();
-    nsort = K;
   }
-  int P = 2;
-  while (P < max(nsort, K)) P <<= 1;
-  for (int i = nsort + tid; i < P; i += BLOCK) sm_row.cand[i] = 0;  // 0: below every real word
+  if (lane == 0) red_c[wid] = wcnt;
   __syncthreads();
-  bitonic_desc<BLOCK>(sm_row.cand, P);
+  int cnt[NW];
+  int ncand = 0, maxc = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    cnt[w] = red_c[w];
+    ncand += cnt[w];
+    maxc = max(maxc, cnt[w]);
+  }
+  const bool over = maxc > SEG;
+  uint64_t* out = PART ? a.part_cand + ((size_t)r * pl.S + sidx) * K : a.row_cand + (size_t)r * K;
+  if (!over && ncand <= BLOCK) {
+    // rank selection: candidate words are distinct (ids differ), so the
+    // number of larger words is the position in descending order
+    if (tid < ncand) {
+      int i = tid, sw = 0;
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) {
+        if (sw == w && i >= cnt[w]) {
+          i -= cnt[w];
+          sw = w + 1;
+        }
+      }
+      const uint64_t word = sm_row.cand[sw * SEG + i];
+      // the segments are read side by side, U words of each per round trip
+      constexpr int U = NW > 4 ? 4 : 8;
+      int rank = 0;
+      for (int j = 0; j < maxc; j += U) {
+        uint64_t v[NW][U];
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int u = 0; u < U; ++u) v[w][u] = sm_row.cand[w * SEG + min(j + u, max(cnt[w] - 1, 0))];
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int u = 0; u < U; ++u) rank += (j + u < cnt[w] && v[w][u] > word) ? 1 : 0;
+      }
+      if (rank < K) out[rank] = word;
+    } else if (tid < K) {
+      out[tid] = 0;  // fewer elements than K: padding below every real word
+    }
+  } else {
+    int nsort;
+    if (!over) {
+      // more candidates than threads: zero the segment tails (0 is below
+      // every real word) and sort the whole buffer
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        for (int i = cnt[w] + tid; i < SEG; i += BLOCK) sm_row.cand[w * SEG + i] = 0;
+      nsort = kCandMax;
+    } else {
+      // Exact fallback (rows with very many near-top ties): find the K-th
+      // largest key bit by bit, then keep the keys above it and the lowest
+      // ids among the keys equal to it.
+      uint32_t t = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        int cnt = 0;
+        view.visit_mem(tid, [&](int, float raw) __attribute__((always_inline)) { cnt += key_of(raw) >= c ? 1 : 0; });
+        if (block_sum<BLOCK>(cnt, red_i) >= K) t = c;
+      }
+      int gt = 0;
+      view.visit_mem(tid, [&](int, float raw) __attribute__((always_inline)) { gt += key_of(raw) > t ? 1 : 0; });
+      const int ngt = block_sum<BLOCK>(gt, red_i);
+      if (tid == 0) s_cnt = 0;
+      __syncthreads();
+      view.visit_mem(tid, [&](int id, float raw) __attribute__((always_inline)) {
+        uint32_t kk = key_of(raw);
+        if (kk > t) sm_row.cand[atomicAdd(&s_cnt, 1)] = cand_word(kk, id);
+      });
+      const int need = K - ngt;
+      int base = 0;
+      const int nc = view.num_chunks();
+      for (int c = 0; c < nc && base < need; ++c) {
+        int local = 0;
+        view.visit_chunk(c, tid, [&](int, float raw) __attribute__((always_inline)) { local += key_of(raw) == t ? 1 : 0; });
+        int excl;
+        const int total = block_exclusive_scan<BLOCK>(local, &excl, red_i);
+        int j = 0;
+        view.visit_chunk(c, tid, [&](int id, float raw) __attribute__((always_inline)) {
+          if (key_of(raw) == t) {
+            if (base + excl + j < need) sm_row.cand[atomicAdd(&s_cnt, 1)] = cand_word(t, id);
+            ++j;
+          }
+        });
+        base += total;
+      }
+      __syncthreads();
+      nsort = K;
+    }
+    int P = 2;
+    while (P < max(nsort, K)) P <<= 1;
+    for (int i = nsort + tid; i < P; i += BLOCK) sm_row.cand[i] = 0;  // 0: below every real word
+    __syncthreads();
+    bitonic_desc<BLOCK>(sm_row.cand, P);
+    if (tid < K) out[tid] = sm_row.cand[tid];
+  }
 
-  // ---- outputs
+  // ---- the row's (chunk's) maximum, status bits and fixed-point sum
   if (PART) {
-    const int q = r * pl.S + sidx;
-    if (tid < K) a.part_cand[(size_t)q * K + tid] = sm_row.cand[tid];
     if (tid == 0) {
+      const int q = r * pl.S + sidx;
       a.part_max[q] = m;
       a.part_flags[q] = flags;
     }
   } else {
-    const uint64_t S = block_sum_u64<BLOCK>((uint64_t)acc, red_u);
-    if (tid < K) a.row_cand[(size_t)r * K + tid] = sm_row.cand[tid];
+    const uint64_t ws = wave_sum_u64_dpp((uint64_t)acc);
+    if (lane == 0) red_u[wid] = ws;
+    __syncthreads();
     if (tid == 0) {
+      uint64_t S = red_u[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) S += red_u[w];
       a.row_max[r] = m;
       a.row_flags[r] = flags | (m == -INFINITY ? 2 : 0);
       a.row_sum[r] = S;
@@ -398,16 +490,75 @@ __global__ __launch_bounds__(BLOCK) void k_rows(BuildArgs a, RowPlan pl) {
   }
 }
 
-// Second pass of a split row: the fixed-point sum of chunk s with the row
-// maximum over all chunks; the workgroup of chunk 0 also merges the chunks'
-// candidate words into the row's K best.
+// Second stage of a split row. Workgroups [0, rows*S): the fixed-point sum
+// of chunk s with the row maximum over all chunks. Workgroups [rows*S,
+// rows*S + rows): the merge of row r's S chunk lists (each its chunk's K best
+// words, best first) into the row's K best, its maximum and status bits.
 template <typename IN_T, int BLOCK, int CH, bool GENERAL>
 __global__ __launch_bounds__(BLOCK) void k_rows_sum(BuildArgs a, RowPlan pl) {
-  __shared__ uint64_t red_u[16];
+  constexpr int NW = BLOCK / 64;
+  __shared__ uint64_t red_u[NW];
+  __shared__ uint64_t cands[512];
+  __shared__ uint64_t s_T;
+  __shared__ int s_cnt;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int K = a.K;
+  const int rows = a.batch * a.L;
+  if ((int)blockIdx.x >= rows * pl.S) {
+    const int r = (int)blockIdx.x - rows * pl.S;
+    const int S = pl.S, q0 = r * S, nw = S * K;  // nw <= 512: two words per thread
+    const uint64_t* pc = a.part_cand + (size_t)q0 * K;
+    const uint64_t w0 = tid < nw ? pc[tid] : 0ull;
+    const uint64_t w1 = tid + BLOCK < nw ? pc[tid + BLOCK] : 0ull;
+    if (tid == 0) s_cnt = 0;
+    if (wid == 0) {
+      // threshold T: the K-th largest of the first qf words of every chunk
+      // (S * qf >= K distinct words, so at least K words are >= T); lane l
+      // holds the l-th of them and counts the larger ones by broadcasts
+      const int qf = (K + S - 1) / S, n1 = S * qf;  // n1 < K + S <= 64
+      const uint64_t f = lane < n1 ? pc[(lane / qf) * K + lane % qf] : 0ull;
+      const uint32_t fh = (uint32_t)(f >> 32), flo = (uint32_t)f;
+      int rank = 0;
+      for (int j = 0; j < n1; ++j) {
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)fh, j) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)flo, j);
+        rank += o > f ? 1 : 0;
+      }
+      const uint64_t hit = __ballot(lane < n1 && rank == K - 1);
+      uint64_t T = 0ull;  // no word of rank K-1 (padding words only): keep all
+      if (hit != 0ull) {
+        const int l = __ffsll((unsigned long long)hit) - 1;
+        T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)fh, l) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)flo, l);
+      }
+      const float m = wave_max_dpp(lane < S ? a.part_max[q0 + lane] : -INFINITY);
+      const uint32_t fl = wave_or_dpp(lane < S ? (uint32_t)a.part_flags[q0 + lane] : 0u);
+      if (lane == 0) {
+        s_T = T;
+        a.row_max[r] = m;
+        a.row_flags[r] = (int)fl | (m == -INFINITY ? 2 : 0);
+      }
+    }
+    __syncthreads();
+    const uint64_t T = s_T;
+    if (w0 >= T && w0 != 0ull) cands[atomicAdd(&s_cnt, 1)] = w0;
+    if (w1 >= T && w1 != 0ull) cands[atomicAdd(&s_cnt, 1)] = w1;
+    __syncthreads();
+    const int nc = s_cnt;
+    for (int i = tid; i < max(nc, K); i += BLOCK) {
+      if (i < nc) {
+        const uint64_t w = cands[i];
+        const int rank = count_greater(cands, nc, w);
+        if (rank < K) a.row_cand[(size_t)r * K + rank] = w;
+      } else {
+        a.row_cand[(size_t)r * K + i] = 0;
+      }
+    }
+    return;
+  }
+
   const int r = (int)blockIdx.x / pl.S;
   const int sidx = (int)blockIdx.x - r * pl.S;
-  const int K = a.K;
   const int mode = GENERAL ? a.mode : 0;
   const float inv_tau = a.inv_tau;
 
@@ -422,48 +573,35 @@ __global__ __launch_bounds__(BLOCK) void k_rows_sum(BuildArgs a, RowPlan pl) {
 
   // row maximum and status bits over the S chunks (S <= 64: one load per lane)
   const int q0 = r * pl.S;
-  const float mc = lane < pl.S ? a.part_max[q0 + lane] : -INFINITY;
-  const float m = wave_max(mc);
+  const float m = wave_max_dpp(lane < pl.S ? a.part_max[q0 + lane] : -INFINITY);
+  const uint32_t fl = wave_or_dpp(lane < pl.S ? (uint32_t)a.part_flags[q0 + lane] : 0u);
 
   double acc = 0.0;
   const bool finite_m = m != -INFINITY;
-  view.visit(tid, [&](int, float raw) __attribute__((always_inline)) {
-    float x = raw;
-    if (GENERAL && mode == 1) x = x * inv_tau;
-    const float xs = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
-    float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
-    d = finite_m ? d : -INFINITY;
-    acc += exp_fixed(d);
-  });
-  const uint64_t S = block_sum_u64<BLOCK>((uint64_t)acc, red_u);
-  if (tid == 0) a.row_sum[(size_t)q0 + sidx] = S;
-
-  if (sidx != 0 || wid != 0) return;
-  // merge: the K best of the S x K chunk words, by repeated wave maxima
-  int fl = lane < pl.S ? a.part_flags[q0 + lane] : 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
-  constexpr int kMaxPer = 8;  // S * K <= 512
-  const int nw = pl.S * K;
-  uint64_t wv[kMaxPer];
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    const int i = lane + 64 * j;
-    wv[j] = i < nw ? a.part_cand[(size_t)q0 * K + i] : 0ull;
+  if (fl == 0 && finite_m && !(GENERAL && mode == 2)) {
+    view.visit(tid, [&](int, float raw) __attribute__((always_inline)) {
+      float x = raw;
+      if (GENERAL && mode == 1) x = x * inv_tau;
+      acc += exp_fixed(x - m);
+    });
+  } else {
+    view.visit(tid, [&](int, float raw) __attribute__((always_inline)) {
+      float x = raw;
+      if (GENERAL && mode == 1) x = x * inv_tau;
+      const float xs = ((x != x) || (x == INFINITY)) ? -INFINITY : x;
+      float d = (GENERAL && mode == 2) ? ((xs == m) ? 0.0f : -INFINITY) : (xs - m);
+      d = finite_m ? d : -INFINITY;
+      acc += exp_fixed(d);
+    });
   }
-  for (int k = 0; k < K; ++k) {
-    uint64_t best = wv[0];
+  const uint64_t ws = wave_sum_u64_dpp((uint64_t)acc);
+  if (lane == 0) red_u[wid] = ws;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t S = red_u[0];
 #pragma unroll
-    for (int j = 1; j < kMaxPer; ++j) best = wv[j] > best ? wv[j] : best;
-    const uint64_t top = wave_max(best);
-    // words are distinct (ids differ), unless both are padding (0)
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) wv[j] = (wv[j] == top && top != 0ull) ? 0ull : wv[j];
-    if (lane == 0) a.row_cand[(size_t)r * K + k] = top;
-  }
-  if (lane == 0) {
-    a.row_max[r] = m;
-    a.row_flags[r] = fl | (m == -INFINITY ? 2 : 0);
+    for (int w = 1; w < NW; ++w) S += red_u[w];
+    a.row_sum[(size_t)q0 + sidx] = S;
   }
 }
 
@@ -510,13 +648,14 @@ hipError_t launch_t(const BuildArgs& a, RowPlan pl, hipStream_t st) {
 // Split rows: 256 threads per chunk, the chunk's vectors in registers.
 template <typename IN_T, int CH>
 hipError_t launch_split(const BuildArgs& a, RowPlan pl, hipStream_t st) {
-  dim3 grid(a.batch * a.L * pl.S), block(256);
+  const int rows = a.batch * a.L;
+  dim3 grid(rows * pl.S), grid2(rows * pl.S + rows), block(256);
   if (a.mode == 0) {
     hipLaunchKernelGGL((k_rows<IN_T, 256, CH, false, true>), grid, block, 0, st, a, pl);
-    hipLaunchKernelGGL((k_rows_sum<IN_T, 256, CH, false>), grid, block, 0, st, a, pl);
+    hipLaunchKernelGGL((k_rows_sum<IN_T, 256, CH, false>), grid2, block, 0, st, a, pl);
   } else {
     hipLaunchKernelGGL((k_rows<IN_T, 256, CH, true, true>), grid, block, 0, st, a, pl);
-    hipLaunchKernelGGL((k_rows_sum<IN_T, 256, CH, true>), grid, block, 0, st, a, pl);
+    hipLaunchKernelGGL((k_rows_sum<IN_T, 256, CH, true>), grid2, block, 0, st, a, pl);
   }
   return hipGetLastError();
 }
@@ -546,7 +685,7 @@ hipError_t launch_dt(const BuildArgs& a, RowPlan pl, hipStream_t st) {
 
 // Rows are split when there are too few of them to give the chip ~512
 // workgroups: S chunks of cv >= 128 vectors each (so no chunk is empty),
-// S <= 32 and S * K <= 512 (the merge holds 8 words per lane).
+// S <= 32 and S * K <= 512 (the merge holds all S * K words in LDS).
 RowPlan plan_rows(int batch, int L, int V, int K, int esize, bool vec_ok) {
   RowPlan pl{1, 0, vec_ok};
   const int rows = batch * L;

@@ -200,3 +200,21 @@ def test_build_all_equal_rows_exact_fallback(B, L, V, K):
         g, _ = gpu_build(x, roots, K, 40, tau)
         o = oracle.build_tree(x, roots, K, 40, tau)
         assert_same_build(g, o)
+
+
+@pytest.mark.parametrize("B,L,V,K,frac", [(1, 2, 151936, 16, 0.08), (16, 16, 20000, 8, 0.06)])
+def test_build_many_tied_candidates(B, L, V, K, frac):
+    """Rows whose top value repeats at a random fraction of positions: more
+    tied candidates than a workgroup has threads, but few enough per wave to
+    stay off the exact fallback, so the full sorting network orders them --
+    inside row chunks (few rows) and on whole rows (many rows). Ties resolve
+    to the lowest token ids."""
+    g = torch.Generator().manual_seed(11)
+    x = (torch.randn((B, L, V), generator=g) * 0.5).to(torch.bfloat16)
+    x[torch.rand((B, L, V), generator=g) < frac] = 4.0
+    roots = list(range(B))
+    for tau in (1.0, 0.0):
+        note("build tied B=%d L=%d V=%d K=%d frac=%g tau=%g" % (B, L, V, K, frac, tau))
+        gb, _ = gpu_build(x, roots, K, 40, tau)
+        o = oracle.build_tree(x, roots, K, 40, tau)
+        assert_same_build(gb, o)
