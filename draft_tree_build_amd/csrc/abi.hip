@@ -174,10 +174,9 @@ int ddtree_accept(const void* target_logits, ddtree_dtype dt, const int32_t* tar
   a.accepted_nodes = accepted_nodes;
   a.accept_len = accept_len;
   a.bonus = bonus;
-  int32_t* ws_tgt;
-  accept_carve(workspace, batch, T, &ws_tgt);
-  a.target_argmax = target_argmax ? target_argmax : ws_tgt;
-  return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
+  a.target_argmax = target_argmax;
+  const AcceptWork w = accept_carve(workspace, batch, T);
+  return hip_status(launch_accept(a, w, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

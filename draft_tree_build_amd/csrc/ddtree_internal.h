@@ -103,11 +103,18 @@ struct AcceptArgs {
   int32_t* accepted_nodes;    // may be null
   int32_t* accept_len;
   int32_t* bonus;
-  int32_t* target_argmax;     // caller output or workspace
+  int32_t* target_argmax;     // may be null
 };
+// Per-chunk arg-max results in the accept workspace: S2 chunks per row.
+struct AcceptWork {
+  int S2;
+  float* pv;
+  int32_t* pidx;
+};
+int accept_splits(int batch, int T);
 size_t accept_workspace_bytes(int batch, int T);
-void accept_carve(void* ws, int batch, int T, int32_t** tgt);
-hipError_t launch_accept(const AcceptArgs& a, hipStream_t stream);
+AcceptWork accept_carve(void* ws, int batch, int T);
+hipError_t launch_accept(const AcceptArgs& a, const AcceptWork& w, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -5,10 +5,16 @@
 // decoding rule; the matched path is accepted and the first unmatched target
 // token becomes the next bonus token. At temperature 0 the rule is argmax.
 //
-// k_argmax: one workgroup per (request, node) row of the target logits,
-// streamed once with 16-byte loads (8 in flight per thread); rows past
-// num_nodes are skipped. k_walk: one wavefront per request, at most L steps,
-// each a ballot over the current node's children.
+// k_argmax: one workgroup per chunk of a (request, node) row of the target
+// logits (S2 chunks per row, so that small batches still fill the chip),
+// streamed once with 16-byte loads; rows past num_nodes are skipped. It
+// leaves the chunk's (maximum, first index) in the workspace. k_walk: one
+// workgroup per request: it reduces the chunk results to the target token of
+// every node, finds for every node its first child carrying that token (all
+// nodes at once), then follows that pointer from the root for at most L
+// steps.
+#include <algorithm>
+
 #include "ddtree_device.h"
 #include "ddtree_internal.h"
 
@@ -16,51 +22,208 @@ namespace ddt {
 namespace {
 
 constexpr int kMaxT = 1025;
+constexpr int kNoChild = 0x7FFFFFFF;
 
 // (value desc, index asc): is (v2, i2) better than (v1, i1)?
 __device__ __forceinline__ bool better(float v2, int i2, float v1, int i1) {
   return v2 > v1 || (v2 == v1 && i2 < i1);
 }
 
-__device__ void walk_wave(const AcceptArgs& a, int b, const int32_t* tgt_row, int32_t* s_tok,
-                          int32_t* s_par, int32_t* s_tgt) {
-  const int lane = threadIdx.x & 63;
-  const int T = a.T;
-  const int nn = min(a.num_nodes[b], T);
-  for (int i = lane; i < T; i += 64) {
-    s_tok[i] = a.tokens[(size_t)b * T + i];
-    s_par[i] = a.parents[(size_t)b * T + i];
-    s_tgt[i] = tgt_row[i];
+// One step of the wave arg-max: the pair CTRL brings in, where better.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = __uint_as_float(dpp_src<CTRL, ROW_MASK>(__float_as_uint(-INFINITY), __float_as_uint(v)));
+  const int oi = (int)dpp_src<CTRL, ROW_MASK>((uint32_t)kNoChild, (uint32_t)i);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  int cur = 0, len = 0, bonus = -1;
-  for (;;) {
-    const int y = s_tgt[cur];
-    int next = -1;
-    for (int c0 = cur + 1; c0 < nn; c0 += 64) {
-      const int c = c0 + lane;
-      const bool hit = c < nn && s_par[c] == cur && s_tok[c] == y;
-      const uint64_t bal = __ballot(hit);
-      if (bal) {
-        next = c0 + __builtin_ctzll(bal);
-        break;
+}
+// Arg-max over the 64 lanes (DPP steps as in dpp_reduce), returned uniform.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<0xB1, 0xF>(v, i);
+  argmax_step<0x4E, 0xF>(v, i);
+  argmax_step<0x141, 0xF>(v, i);
+  argmax_step<0x140, 0xF>(v, i);
+  argmax_step<0x142, 0xA>(v, i);
+  argmax_step<0x143, 0xC>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// Chunk s of row (b, i): blockIdx.x = row * S2 + s. Writes the chunk's
+// maximum and first maximal index (NaN counts as -inf; a chunk of only
+// -inf / NaN reports its first index, an empty chunk index kNoChild).
+template <typename IN_T, int BLOCK, bool VEC, int U>
+__global__ __launch_bounds__(BLOCK) void k_argmax(AcceptArgs a, int S2, float* pv, int32_t* pidx) {
+  constexpr int NW = BLOCK / 64;
+  __shared__ float s_v[NW];
+  __shared__ int s_i[NW];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int T = a.T;
+  const int rowi = (int)blockIdx.x / S2, s = (int)blockIdx.x - rowi * S2;
+  const int b = rowi / T, i = rowi - b * T;
+  if (i >= min(a.num_nodes[b], T)) return;  // no node: the walk never reads it
+  const IN_T* row = static_cast<const IN_T*>(a.target_logits) + (size_t)rowi * a.V;
+  float best = -INFINITY;
+  int bi = kNoChild;
+  if constexpr (VEC) {
+    constexpr int EPV = 16 / sizeof(IN_T);  // U: 16-byte loads in flight per thread
+    const int nvec = a.V / EPV;
+    const int cv = (nvec + S2 - 1) / S2;
+    const int v0 = s * cv, v1 = min(v0 + cv, nvec);
+    const uint4* p = reinterpret_cast<const uint4*>(row);
+    if (v0 + tid < v1) bi = (v0 + tid) * EPV;
+    for (int base = v0 + tid; base < v1; base += BLOCK * U) {
+      uint4 u[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) u[j] = p[min(base + j * BLOCK, v1 - 1)];  // clamped: always in bounds
+      // all U loads are issued before the first use (keeps the compiler
+      // from sinking each load into the guarded block that consumes it)
+#pragma unroll
+      for (int j = 0; j < U; ++j) asm volatile("" : "+v"(u[j].x), "+v"(u[j].y), "+v"(u[j].z), "+v"(u[j].w));
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int vi = base + j * BLOCK;
+        if (vi >= v1) break;
+        const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+        if constexpr (sizeof(IN_T) == 2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x0 = __uint_as_float(w[q] << 16);
+            const float x1 = __uint_as_float(w[q] & 0xFFFF0000u);
+            if (x0 > best) { best = x0; bi = vi * EPV + 2 * q; }
+            if (x1 > best) { best = x1; bi = vi * EPV + 2 * q + 1; }
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x = __uint_as_float(w[q]);
+            if (x > best) { best = x; bi = vi * EPV + q; }
+          }
+        }
       }
     }
-    if (next < 0 || len >= a.L) {
-      bonus = y;
-      break;
+  } else {
+    const int ce = (a.V + S2 - 1) / S2;
+    const int e0 = s * ce, e1 = min(e0 + ce, a.V);
+    if (e0 + tid < e1) bi = e0 + tid;
+    for (int v = e0 + tid; v < e1; v += BLOCK) {
+      float x;
+      if constexpr (sizeof(IN_T) == 2) x = bf16_to_float(reinterpret_cast<const uint16_t*>(row)[v]);
+      else x = reinterpret_cast<const float*>(row)[v];
+      if (x > best) { best = x; bi = v; }
     }
-    if (lane == 0) {
-      a.accepted[(size_t)b * a.L + len] = y;
-      if (a.accepted_nodes) a.accepted_nodes[(size_t)b * a.L + len] = next;
+  }
+  wave_argmax(best, bi);
+  if (lane == 0) {
+    s_v[wid] = best;
+    s_i[wid] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float bv = s_v[0];
+    int bx = s_i[0];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2)
+      if (better(s_v[w2], s_i[w2], bv, bx)) { bv = s_v[w2]; bx = s_i[w2]; }
+    pv[blockIdx.x] = bv;
+    pidx[blockIdx.x] = bx;
+  }
+}
+
+// One workgroup per request (BLOCK >= T where possible: each node's inputs
+// are fetched in one round trip). IDS: target tokens from target_ids; else
+// from the S2 chunk results per row of k_argmax.
+template <bool IDS, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_walk(AcceptArgs a, int S2, const float* pv,
+                                                const int32_t* pidx) {
+  __shared__ int32_t s_tok[kMaxT], s_par[kMaxT], s_tgt[kMaxT], s_next[kMaxT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int b = blockIdx.x;
+  const int T = a.T;
+  const int nn = min(a.num_nodes[b], T);
+  const size_t r0 = (size_t)b * T;
+  for (int i = tid; i < T; i += BLOCK) {
+    const int32_t tk = a.tokens[r0 + i], pa = a.parents[r0 + i];
+    int y = -1;
+    if (i < nn) {
+      if constexpr (!IDS) {
+        // all S2 <= 16 chunk results are requested before the first compare
+        const size_t q = (r0 + i) * S2;
+        float cv[16];
+        int ci[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          cv[s] = s < S2 ? pv[q + s] : -INFINITY;
+          ci[s] = s < S2 ? pidx[q + s] : kNoChild;
+        }
+        float bv = cv[0];
+        int bx = ci[0];
+#pragma unroll
+        for (int s = 1; s < 16; ++s)
+          if (better(cv[s], ci[s], bv, bx)) { bv = cv[s]; bx = ci[s]; }
+        y = bx;
+      } else {
+        y = a.target_ids[r0 + i];
+      }
     }
-    ++len;
-    cur = next;
+    if (a.target_argmax) a.target_argmax[r0 + i] = y;
+    s_tgt[i] = y;
+    s_tok[i] = tk;
+    s_par[i] = pa;
+    s_next[i] = kNoChild;
+  }
+  __syncthreads();
+  // the first child (lowest index) of every node whose token is the node's
+  // target token; a parent index not below the child's (malformed) is skipped
+  for (int c = 1 + tid; c < nn; c += BLOCK) {
+    const int p = s_par[c];
+    if (p >= 0 && p < c && s_tok[c] == s_tgt[p]) atomicMin(&s_next[p], c);
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  int32_t* acc = a.accepted + (size_t)b * a.L;
+  int32_t* accn = a.accepted_nodes ? a.accepted_nodes + (size_t)b * a.L : nullptr;
+  int cur = 0, len = 0, bonus;
+  if (T <= 128) {
+    // small trees: next and target of node j sit in lane j % 64 of two
+    // registers, so each step is a pair of lane reads (no LDS round trip)
+    const int n0 = s_next[lane], t0 = s_tgt[lane];
+    const int n1 = lane + 64 < T ? s_next[lane + 64] : kNoChild;
+    const int t1 = lane + 64 < T ? s_tgt[lane + 64] : -1;
+    for (;;) {
+      const int nx = cur < 64 ? __builtin_amdgcn_readlane(n0, cur) : __builtin_amdgcn_readlane(n1, cur - 64);
+      const int y = cur < 64 ? __builtin_amdgcn_readlane(t0, cur) : __builtin_amdgcn_readlane(t1, cur - 64);
+      if (nx == kNoChild || len >= a.L) {
+        bonus = y;
+        break;
+      }
+      if (lane == 0) {
+        acc[len] = y;
+        if (accn) accn[len] = nx;
+      }
+      ++len;
+      cur = nx;
+    }
+  } else {
+    for (;;) {
+      const int nx = s_next[cur], y = s_tgt[cur];
+      if (nx == kNoChild || len >= a.L) {
+        bonus = y;
+        break;
+      }
+      if (lane == 0) {
+        acc[len] = y;
+        if (accn) accn[len] = nx;
+      }
+      ++len;
+      cur = nx;
+    }
   }
   for (int k = len + lane; k < a.L; k += 64) {
-    a.accepted[(size_t)b * a.L + k] = -1;
-    if (a.accepted_nodes) a.accepted_nodes[(size_t)b * a.L + k] = -1;
+    acc[k] = -1;
+    if (accn) accn[k] = -1;
   }
   if (lane == 0) {
     a.accept_len[b] = len;
@@ -68,134 +231,60 @@ __device__ void walk_wave(const AcceptArgs& a, int b, const int32_t* tgt_row, in
   }
 }
 
-template <typename IN_T, int BLOCK, bool VEC>
-__global__ __launch_bounds__(BLOCK) void k_argmax(AcceptArgs a) {
-  __shared__ float s_v[BLOCK / 64];
-  __shared__ int s_i[BLOCK / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int T = a.T;
-  const int rowi = blockIdx.x;
-  const int b = rowi / T, i = rowi - (rowi / T) * T;
-  const int nn = min(a.num_nodes[b], T);
-  int32_t* tgt = a.target_argmax;
-
-  if (i < nn) {
-    const IN_T* row = static_cast<const IN_T*>(a.target_logits) + (size_t)rowi * a.V;
-    float best = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    if constexpr (VEC) {
-      constexpr int EPV = 16 / sizeof(IN_T);
-      constexpr int U = 8;  // 16-byte loads in flight per thread
-      const int nvec = a.V / EPV;
-      const uint4* p = reinterpret_cast<const uint4*>(row);
-      if (tid < nvec) bi = tid * EPV;
-      for (int base = tid; base < nvec; base += BLOCK * U) {
-        uint4 u[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) u[j] = p[min(base + j * BLOCK, nvec - 1)];  // clamped: always in bounds
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-          const int vi = base + j * BLOCK;
-          if (vi >= nvec) break;
-          const uint32_t w[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
-          if constexpr (sizeof(IN_T) == 2) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float x0 = __uint_as_float(w[q] << 16);
-              const float x1 = __uint_as_float(w[q] & 0xFFFF0000u);
-              if (x0 > best) { best = x0; bi = vi * EPV + 2 * q; }
-              if (x1 > best) { best = x1; bi = vi * EPV + 2 * q + 1; }
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float x = __uint_as_float(w[q]);
-              if (x > best) { best = x; bi = vi * EPV + q; }
-            }
-          }
-        }
-      }
-    } else {
-      if (tid < a.V) bi = tid;
-      for (int v = tid; v < a.V; v += BLOCK) {
-        float x;
-        if constexpr (sizeof(IN_T) == 2) x = bf16_to_float(reinterpret_cast<const uint16_t*>(row)[v]);
-        else x = reinterpret_cast<const float*>(row)[v];
-        if (x > best) { best = x; bi = v; }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
-    }
-    if (lane == 0) { s_v[wid] = best; s_i[wid] = bi; }
-    __syncthreads();
-    if (tid == 0) {
-      float bv = s_v[0];
-      int bx = s_i[0];
-      for (int w2 = 1; w2 < BLOCK / 64; ++w2)
-        if (better(s_v[w2], s_i[w2], bv, bx)) { bv = s_v[w2]; bx = s_i[w2]; }
-      tgt[rowi] = bx;
-    }
-  } else if (tid == 0) {
-    tgt[rowi] = -1;
-  }
-
-}
-
-// Walk only, from given target ids.
-__global__ __launch_bounds__(64) void k_walk_ids(AcceptArgs a) {
-  __shared__ int32_t s_tok[kMaxT], s_par[kMaxT], s_tgt[kMaxT];
-  const int b = blockIdx.x;
-  const int nn = min(a.num_nodes[b], a.T);
-  if (a.target_argmax) {
-    for (int i = threadIdx.x; i < a.T; i += 64)
-      a.target_argmax[(size_t)b * a.T + i] = i < nn ? a.target_ids[(size_t)b * a.T + i] : -1;
-  }
-  walk_wave(a, b, a.target_ids + (size_t)b * a.T, s_tok, s_par, s_tgt);
-}
-
-// The walk of one request from its per-node target tokens.
-__global__ __launch_bounds__(64) void k_walk(AcceptArgs a) {
-  __shared__ int32_t s_tok[kMaxT], s_par[kMaxT], s_tgt[kMaxT];
-  const int b = blockIdx.x;
-  walk_wave(a, b, a.target_argmax + (size_t)b * a.T, s_tok, s_par, s_tgt);
-}
-
 template <typename IN_T>
-hipError_t launch_logits(const AcceptArgs& a, hipStream_t st) {
+hipError_t launch_logits(const AcceptArgs& a, const AcceptWork& w, hipStream_t st) {
   const bool vec = (reinterpret_cast<uintptr_t>(a.target_logits) % 16 == 0) &&
                    ((size_t)a.V * sizeof(IN_T)) % 16 == 0;
-  dim3 grid(a.batch * a.T);
-  if (vec)
-    hipLaunchKernelGGL((k_argmax<IN_T, 256, true>), grid, dim3(256), 0, st, a);
+  dim3 grid(a.batch * a.T * w.S2);
+  const int cv = (int)(((size_t)a.V * sizeof(IN_T) / 16 + w.S2 - 1) / w.S2);  // vectors per chunk
+  if (!vec)
+    hipLaunchKernelGGL((k_argmax<IN_T, 256, false, 1>), grid, dim3(256), 0, st, a, w.S2, w.pv, w.pidx);
+  else if (cv >= 8 * 256)
+    hipLaunchKernelGGL((k_argmax<IN_T, 256, true, 8>), grid, dim3(256), 0, st, a, w.S2, w.pv, w.pidx);
   else
-    hipLaunchKernelGGL((k_argmax<IN_T, 256, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_argmax<IN_T, 256, true, 2>), grid, dim3(256), 0, st, a, w.S2, w.pv, w.pidx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_walk, dim3(a.batch), dim3(64), 0, st, a);
+  if (a.T <= 256)
+    hipLaunchKernelGGL((k_walk<false, 256>), dim3(a.batch), dim3(256), 0, st, a, w.S2, w.pv, w.pidx);
+  else
+    hipLaunchKernelGGL((k_walk<false, 1024>), dim3(a.batch), dim3(1024), 0, st, a, w.S2, w.pv, w.pidx);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t accept_workspace_bytes(int batch, int T) { return align_up((size_t)batch * T * 4, 256); }
-
-void accept_carve(void* ws, int batch, int T, int32_t** tgt) {
-  (void)batch;
-  (void)T;
-  *tgt = reinterpret_cast<int32_t*>(ws);
+// Chunks per target row: enough workgroups (about 512) to fill the chip when
+// the batch has few tree nodes, at most 16.
+int accept_splits(int batch, int T) {
+  const long long rows = (long long)batch * T;
+  return (int)std::min<long long>(16, std::max<long long>(1, (512 + rows - 1) / rows));
 }
 
-hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {
+size_t accept_workspace_bytes(int batch, int T) {
+  const size_t parts = (size_t)batch * T * accept_splits(batch, T);
+  return 2 * align_up(parts * 4, 256);
+}
+
+AcceptWork accept_carve(void* ws, int batch, int T) {
+  AcceptWork w;
+  w.S2 = accept_splits(batch, T);
+  const size_t parts = (size_t)batch * T * w.S2;
+  w.pv = reinterpret_cast<float*>(ws);
+  w.pidx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(parts * 4, 256));
+  return w;
+}
+
+hipError_t launch_accept(const AcceptArgs& a, const AcceptWork& w, hipStream_t st) {
   if (!a.target_logits) {
-    hipLaunchKernelGGL(k_walk_ids, dim3(a.batch), dim3(64), 0, st, a);
+    if (a.T <= 256)
+      hipLaunchKernelGGL((k_walk<true, 256>), dim3(a.batch), dim3(256), 0, st, a, 0, nullptr, nullptr);
+    else
+      hipLaunchKernelGGL((k_walk<true, 1024>), dim3(a.batch), dim3(1024), 0, st, a, 0, nullptr, nullptr);
     return hipGetLastError();
   }
-  if (a.dtype == 0) return launch_logits<uint16_t>(a, st);
-  return launch_logits<float>(a, st);
+  if (a.dtype == 0) return launch_logits<uint16_t>(a, w, st);
+  return launch_logits<float>(a, w, st);
 }
 
 }  // namespace ddt

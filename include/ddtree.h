@@ -165,7 +165,9 @@ int ddtree_verify_attn(const void *q, const void *k, const void *v, ddtree_dtype
  *   bonus           [batch] int32                         out
  *   target_argmax   [batch, T] int32 or NULL              out: the target token
  *                   per node (-1 for rows >= num_nodes[b])
- *   workspace       >= ddtree_accept_workspace_size(...) bytes
+ *   workspace       >= ddtree_accept_workspace_size(...) bytes: per-chunk
+ *                   arg-max results (rows are split into up to 16 chunks
+ *                   when batch * T is small)
  * Limits: T <= 1025, 1 <= L <= 64, V <= 2^31 - 1 (logits path: V >= 1).
  */
 size_t ddtree_accept_workspace_size(int batch, int T);

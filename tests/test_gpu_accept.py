@@ -103,3 +103,27 @@ def test_accept_full_size_workloads(name):
     g = _gpu_accept(tl, None, tree, w.L)
     o = oracle.accept(tl, None, tree["tokens"], tree["parents"], tree["num_nodes"], w.L)
     _same(g, o)
+
+
+def test_accept_optional_outputs_absent():
+    """target_argmax and accepted_nodes may be NULL: the walk still runs from
+    the per-node target tokens, which then stay in the workgroup."""
+    B, L, V, K, N = 4, 7, 3000, 6, 90
+    g = torch.Generator().manual_seed(3)
+    tree = oracle.build_tree(torch.randn(B, L, V, generator=g) * 2, [0, 1, 2, 3], K, N, 1.0)
+    tl = _planted_logits(tree, V, torch.bfloat16, seed=3, follow=0.9)
+    o = oracle.accept(tl, None, tree["tokens"], tree["parents"], tree["num_nodes"], L)
+    tok = torch.from_numpy(tree["tokens"]).to(DEV)
+    par = torch.from_numpy(tree["parents"]).to(DEV)
+    nn = torch.from_numpy(tree["num_nodes"]).to(DEV)
+    T = tok.shape[1]
+    i32 = dict(dtype=torch.int32, device=DEV)
+    acc, alen, bonus = torch.empty(B, L, **i32), torch.empty(B, **i32), torch.empty(B, **i32)
+    ws = api.new_workspace(api.ddtree_accept_workspace_size(B, T), DEV)
+    note("accept without optional outputs")
+    api.ddtree_accept(tl.to(DEV), None, tok, par, nn, L, acc, None, alen, bonus, None, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), o["accepted"])
+    np.testing.assert_array_equal(alen.cpu().numpy(), o["accept_len"])
+    np.testing.assert_array_equal(bonus.cpu().numpy(), o["bonus"])
+    assert o["accept_len"].max() >= 2
