@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   const int Rpad = row_tiles * kTileRows;
   const size_t bh = (size_t)bhi;
   const size_t nbh = (size_t)a.batch * a.Hkv;
-  {
+  if (row_valid) {  // rows past num_nodes are zeroed by the merge, which never reads them
     float* po = part_o + (((size_t)z * nbh + bh) * Rpad + row) * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -388,79 +388,76 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   }
 }
 
-// Merge of the split partials: 32 query rows of one (request, kv-head) per
-// workgroup. Per row, the split weights w_z = 2^(m_z - M) / sum_z 2^(m_z - M) l_z
-// go to LDS; then each output chunk sums w_z O_z with several partial loads
-// in flight per thread.
+// Merge of the split partials: 8 query rows of one (request, kv-head) per
+// workgroup, one 16-byte output chunk per thread. Per row, the split weights
+// are w_z = 2^(m_z - M) / sum_z 2^(m_z - M) l_z (M = max_z m_z); each thread
+// requests its row's (m_z, l_z) and its chunk of every O_z together (eight
+// splits per round trip), computes the weights itself and sums w_z O_z.
+// Rows past num_nodes have no partials: they are written as zeros.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int nsplit, int row_tiles,
                                                       const float* part_o, const float* part_ml) {
-  constexpr int kRows = 32;
-  __shared__ float wts[kRows * 32];  // nsplit <= 32
+  constexpr int kRows = 8;
+  constexpr int kU = 8;  // splits per round trip
   const int tid = threadIdx.x;
+  const int rl = tid >> 5, c4 = tid & 31;
   const int b = blockIdx.y / a.Hkv, hk = blockIdx.y - (blockIdx.y / a.Hkv) * a.Hkv;
   const int g = a.Hq / a.Hkv;
   const int T = a.T;
   const int R = T * g;
+  const int rr = blockIdx.x * kRows + rl;
+  if (rr >= R) return;
   const int nn = min(max(a.num_nodes[b], 0), T);
-  const int nvalid_rows = nn * g;
-  const int r0 = blockIdx.x * kRows;
+  const int nd = rr / g, hd = hk * g + (rr - nd * g);
+  uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * T + nd) * a.Hq + hd) * kD + 4 * c4;
+  if (rr >= nn * g) {
+    *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
   const int Rpad = row_tiles * kTileRows;
   const size_t bh = (size_t)b * a.Hkv + hk;
   const size_t nbh = (size_t)a.batch * a.Hkv;
-  uint16_t* O = static_cast<uint16_t*>(a.out);
-  // split maxima and sums of the 32 rows, all loads in flight at once
-  __shared__ float sm[kRows * 32], sl[kRows * 32];
-  const size_t zstride = nbh * Rpad * 2;
-  for (int idx = tid; idx < kRows * nsplit; idx += 256) {
-    const int rl = idx / nsplit, zz = idx - rl * nsplit;
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (bh * Rpad + r0 + rl) * 2 + zz * zstride);
-    sm[idx] = ml.x;
-    sl[idx] = ml.y;
-  }
-  __syncthreads();
-  if (tid < kRows) {
-    const int rr = r0 + tid;
-    float M = -INFINITY;
-    for (int zz = 0; zz < nsplit; ++zz) M = fmaxf(M, sm[tid * nsplit + zz]);
-    float den = 0.f;
-    for (int zz = 0; zz < nsplit; ++zz)
-      den += (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[tid * nsplit + zz] - M) * sl[tid * nsplit + zz];
-    const float inv = (den > 0.f && rr < nvalid_rows) ? 1.0f / den : 0.0f;
-    for (int zz = 0; zz < nsplit; ++zz)
-      wts[tid * nsplit + zz] = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm[tid * nsplit + zz] - M) * inv;
-  }
-  __syncthreads();
-  constexpr int kU = 8;
-  for (int idx = tid; idx < kRows * (kD / 4); idx += 256) {
-    const int rl = idx / (kD / 4), c4 = idx - rl * (kD / 4);
-    const int rr = r0 + rl;
-    if (rr >= R) continue;
-    const int nd = rr / g, hd = hk * g + (rr - nd * g);
-    const size_t pbase = (bh * Rpad + rr) * kD + 4 * c4;
-    const size_t pstride = nbh * Rpad * kD;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int z0 = 0; z0 < nsplit; z0 += kU) {
-      float4 oz[kU];
+  const size_t pbase = (bh * Rpad + rr) * kD + 4 * c4, pstride = nbh * Rpad * kD;
+  const size_t mbase = (bh * Rpad + rr) * 2, mstride = nbh * Rpad * 2;
+  // running merge over groups of kU splits (one group when nsplit <= kU)
+  float M = -INFINITY, den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int z0 = 0; z0 < nsplit; z0 += kU) {
+    float2 ml[kU];
+    float4 oz[kU];
 #pragma unroll
-      for (int j = 0; j < kU; ++j) {
-        const int zz = min(z0 + j, nsplit - 1);
-        oz[j] = *reinterpret_cast<const float4*>(part_o + pbase + zz * pstride);
-      }
-#pragma unroll
-      for (int j = 0; j < kU; ++j) {
-        const float wz = (z0 + j < nsplit) ? wts[rl * nsplit + z0 + j] : 0.f;
-        acc.x += wz * oz[j].x;
-        acc.y += wz * oz[j].y;
-        acc.z += wz * oz[j].z;
-        acc.w += wz * oz[j].w;
-      }
+    for (int j = 0; j < kU; ++j) {
+      const int zz = min(z0 + j, nsplit - 1);
+      ml[j] = *reinterpret_cast<const float2*>(part_ml + mbase + zz * mstride);
+      oz[j] = *reinterpret_cast<const float4*>(part_o + pbase + zz * pstride);
     }
-    floatx2 lo2 = {acc.x, acc.y}, hi2 = {acc.z, acc.w};
-    bf16x2 l2 = __builtin_convertvector(lo2, bf16x2);
-    bf16x2 h2 = __builtin_convertvector(hi2, bf16x2);
-    bf16x4 o4 = {l2[0], l2[1], h2[0], h2[1]};
-    *reinterpret_cast<bf16x4*>(O + (((size_t)b * T + nd) * a.Hq + hd) * kD + 4 * c4) = o4;
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (z0 + j < nsplit) Mg = fmaxf(Mg, ml[j].x);
+    if (Mg == -INFINITY) continue;  // no key reached this row yet
+    const float sc = __builtin_amdgcn_exp2f(M - Mg);  // rescale of the groups before
+    den *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const float e = (z0 + j < nsplit) ? __builtin_amdgcn_exp2f(ml[j].x - Mg) : 0.f;
+      den += e * ml[j].y;
+      acc.x += e * oz[j].x;
+      acc.y += e * oz[j].y;
+      acc.z += e * oz[j].z;
+      acc.w += e * oz[j].w;
+    }
+    M = Mg;
   }
+  const float inv = den > 0.f ? 1.0f / den : 0.0f;
+  floatx2 lo2 = {acc.x * inv, acc.y * inv}, hi2 = {acc.z * inv, acc.w * inv};
+  bf16x2 l2 = __builtin_convertvector(lo2, bf16x2);
+  bf16x2 h2 = __builtin_convertvector(hi2, bf16x2);
+  bf16x4 o4 = {l2[0], l2[1], h2[0], h2[1]};
+  *reinterpret_cast<bf16x4*>(o) = o4;
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -620,7 +617,7 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s.nsplit <= 1) return e;
   const int R = a.T * (a.Hq / a.Hkv);
-  dim3 cgrid((R + 31) / 32, a.batch * a.Hkv);
+  dim3 cgrid((R + 7) / 8, a.batch * a.Hkv);
   hipLaunchKernelGGL(k_attn_combine, cgrid, block, 0, st, a, s.nsplit, s.row_tiles,
                      (const float*)part_o, (const float*)part_ml);
   return hipGetLastError();
