@@ -213,7 +213,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   auto load_mword = [&](int t) __attribute__((always_inline)) -> uint64_t {
     return (t >= np && row_valid) ? mrow[t - np] : 0ull;
   };
-  // One key tile from LDS (kl, vl: the tile's K and V buffers).
+  // One key tile from LDS (kl, vl: the tile's K and V buffers). Both 32-key
+  // halves of S^T are computed first (two independent MFMA chains), the
+  // online softmax then covers the whole tile (one maximum update), and the
+  // exponentials of the second half run on the VALU while the first half's
+  // O^T += V^T P^T products occupy the matrix core.
   auto tile_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl)
       __attribute__((always_inline)) {
     int base, nvalid;
@@ -224,20 +228,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     uint64_t allow = nvalid >= kKeys ? ~0ull : ((1ull << nvalid) - 1ull);
     if (tree_tile) allow &= mword;
 
-    // ---- two halves of 32 keys: S^T = K Q^T, online softmax, O^T += V^T P^T
+    // ---- S^T = K Q^T for keys 0..31 (sc[0]) and 32..63 (sc[1])
+    floatx16 sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 kf[8];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        kf[ks] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + kb * 32 * 256);
-      floatx16 sc;
+      for (int v = 0; v < 16; ++v) sc[kb][v] = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sc[v] = 0.0f;
+    for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
-      // V fragments of this half, read while the scores are computed
-      bf16x8 vf[4][2];
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + kb * 32 * 256);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
+      }
+    }
+    // V fragments of the first half, read while the scores are computed
+    auto read_v = [&](int kb, bf16x8 (&vf)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -247,40 +253,59 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
           const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][1] + kofs));
           vf[db][hf] = __builtin_bit_cast(bf16x8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
         }
-      // mask (tree tiles and the ragged last prefix tile only) and row max.
-      // Query rows past num_nodes need no masking: their scores never reach
-      // a valid row and their outputs are written as zeros.
-      float tmax = -INFINITY;
+    };
+    bf16x8 vf[4][2];
+    read_v(0, vf);
+
+    // ---- mask (tree tiles and the ragged last prefix tile only) and row max.
+    // Query rows past num_nodes need no masking: their scores never reach a
+    // valid row and their outputs are written as zeros.
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       if (need_mask) {
         // register v holds key 32 kb + 8 gq + v (v < 8) or + 8 more (v >= 8)
         const uint32_t sh = 32 * kb + 8 * gq;
         const uint32_t bits = (uint32_t)((allow >> sh) & 0xFFull) | ((uint32_t)((allow >> (sh + 16)) & 0xFFull) << 8);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          sc[v] = ((bits >> v) & 1u) ? sc[v] : -INFINITY;
-          tmax = fmaxf(tmax, sc[v]);
+          sc[kb][v] = ((bits >> v) & 1u) ? sc[kb][v] : -INFINITY;
+          tmax = fmaxf(tmax, sc[kb][v]);
         }
       } else {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[kb][v]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax * c_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      // P is carried as a pair of bf16 MFMA operands, P = hi + lo with
-      // hi = bf16(p) and lo = bf16(p - hi): |p - hi - lo| <= 2^-18 p, so the
-      // weights keep ~fp32 accuracy even when only a few keys contribute.
-      float psum = 0.0f;
-      bf16x8 pf[2], pl[2];
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // The reference m_run of the exponentials moves only when a row's
+    // maximum passes it by more than 8 (log2 units): weights then stay below
+    // 2^8, and O and l are rescaled on few tiles (O and l share the
+    // reference, so the final O / l is unchanged).
+    const float m_new = fmaxf(m_run, tmax * c_log2);
+    float alpha = 1.0f;
+    if (__ballot(m_new > m_run + 8.0f) != 0) {
+      alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.0f : m_new));
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+    // P is carried as a pair of bf16 MFMA operands, P = hi + lo with
+    // hi = bf16(p) and lo = bf16(p - hi): |p - hi - lo| <= 2^-18 p, so the
+    // weights keep ~fp32 accuracy even when only a few keys contribute.
+    float psum = 0.0f;
+    auto probs = [&](int kb, bf16x8 (&pf)[2], bf16x8 (&pl)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         bf16x2 hi2[4], lo2[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           floatx2 pr;
-          pr[0] = __builtin_amdgcn_exp2f(fmaf(sc[8 * hf + 2 * e2], c_log2, -m_use));
-          pr[1] = __builtin_amdgcn_exp2f(fmaf(sc[8 * hf + 2 * e2 + 1], c_log2, -m_use));
+          pr[0] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2], c_log2, -m_use));
+          pr[1] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2 + 1], c_log2, -m_use));
           psum += pr[0] + pr[1];
           hi2[e2] = __builtin_convertvector(pr, bf16x2);
           const uint32_t hb = __builtin_bit_cast(uint32_t, hi2[e2]);
@@ -292,23 +317,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
         pl[hf] = bf16x8{lo2[0][0], lo2[0][1], lo2[1][0], lo2[1][1],
                         lo2[2][0], lo2[2][1], lo2[3][0], lo2[3][1]};
       }
-      l_run = l_run * alpha + psum;
-      // the running max settles after a few tiles: rescale O only when it moved
-      if (__ballot(m_new != m_run) != 0) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-      }
-      m_run = m_new;
+    };
+    auto pv = [&](const bf16x8 (&vfr)[4][2], const bf16x8 (&pf)[2], const bf16x8 (&pl)[2])
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][hf], pf[hf], acc_o[db], 0, 0, 0);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][hf], pl[hf], acc_o[db], 0, 0, 0);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[db][hf], pl[hf], acc_o[db], 0, 0, 0);
         }
-    }
+    };
+    bf16x8 pf0[2], pl0[2];
+    probs(0, pf0, pl0);
+    pv(vf, pf0, pl0);
+    bf16x8 pf1[2], pl1[2];
+    probs(1, pf1, pl1);
+    read_v(1, vf);
+    pv(vf, pf1, pl1);
+    l_run = l_run * alpha + psum;
   };
 
   // Tiles alternate between two LDS buffers (static, so that the compiler

@@ -32,6 +32,8 @@ constexpr int kBlock = 256;
 constexpr int kShl1 = 0x130;    // DPP wave_shl:1  lane i reads lane i + 1
 constexpr int kShr1 = 0x138;    // DPP wave_shr:1  lane i reads lane i - 1
 
+typedef float floatx32 __attribute__((ext_vector_type(32)));
+
 struct TreeShared {
   int32_t tok[kMaxLK];          // top-K tokens per position, [L, K]
   float lp[kMaxLK + 2];         // their log-probabilities (+2: reads past the last row)
@@ -107,11 +109,12 @@ __device__ void sort_over(TreeShared& sh, int count) {
 // of a key is the score's bit pattern itself (+0 -> 0, -inf -> 0xFF800000,
 // 0xFFFFFFFF marks "no candidate").
 //
-// A pending candidate is (key, ps, ss): ps is its parent's score and ss the
-// score of its next sibling (ps + lp at the next rank), or the marker when it
-// has none. Popping candidate (d, p, r) yields
-//   sibling (d, p, r+1): score ss, next-sibling score ps + lp[d-1][r+2]
-//   child (d+1, n, 0):   score s + lp[d][0], next-sibling score s + lp[d][1]
+// A pending candidate is (key, ps): ps is its parent's score. Popping
+// candidate (d, p, r) with score s yields
+//   sibling (d, p, r+1): score ps + lp[d-1][r+1] (when rank r+1 exists)
+//   child (d+1, n, 0):   score s + lp[d][0]
+// -- the log-probability table sits in registers (lane d, element k holds
+// lp[d][k]), so each is one indexed register move and one lane read --
 // and the lane array is rebuilt from the old lanes shifted by -1, 0 or +1
 // plus the two new candidates c1 < c2, lane j taking
 //   old j+1 if it precedes c1 | c1 | old j if between | c2 | old j-1.
@@ -126,19 +129,16 @@ constexpr uint32_t kNone = 0xFFFFFFFFu;
 template <bool SIB>
 __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
   const int lane = threadIdx.x & 63;
-  // lane d: lp of the best and second-best token at position d, and the LDS
-  // byte offset of lp[d][2]
-  const float tb0 = lane < L ? sh.lp[lane * K] : 0.0f;
-  const float tb1 = (SIB && lane < L) ? sh.lp[lane * K + 1] : 0.0f;
-  const uint32_t rowoff = (uint32_t)((lane * K + 2) * 4);
+  floatx32 tbl;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) tbl[k] = (lane < L && k < K) ? sh.lp[lane * K + k] : 0.0f;
   const uint32_t rank_lim = (uint32_t)K << 9;  // rank field limit
 
-  uint32_t Hh = kNone, Hl = kNone, Hps = 0u, Hss = kNone;
+  uint32_t Hh = kNone, Hl = kNone, Hps = 0u;
   if (lane == 0) {  // the root's best child: depth 1, parent 0, rank 0
     Hh = __float_as_uint(0.0f + sh.lp[0]);
     Hl = key_lo(1, 0, 0);
     Hps = __float_as_uint(0.0f);
-    Hss = SIB ? __float_as_uint(0.0f + sh.lp[1]) : kNone;
   }
   uint32_t rec_h = 0u, rec_l = 0u;  // popped keys, node i in lane i % 64 (node 0: root)
   int h = 1;
@@ -149,34 +149,28 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
   // One pop; OVER: keep candidates behind the lanes in the overflow list.
   auto pop = [&](auto over_tag) __attribute__((always_inline)) {
     constexpr bool OVER = decltype(over_tag)::value;
-    const uint32_t xh = rdlane(Hh, 0), xl = rdlane(Hl, 0), xps = rdlane(Hps, 0),
-                   xss = rdlane(Hss, 0);
+    const uint32_t xh = rdlane(Hh, 0), xl = rdlane(Hl, 0), xps = rdlane(Hps, 0);
     rec_h = wrlane(rec_h, xh, (uint32_t)(n & 63));
     rec_l = wrlane(rec_l, xl, (uint32_t)(n & 63));
     if ((n & 63) == 63) sh.nkey[(n & ~63) + lane] = key64(rec_h, rec_l);
     const int d = (int)(xl >> 25);     // 1..L
     const int dc = d & 63;             // lane of position d (unused when d == L == 64)
     const uint32_t rf = xl & 0x3E00u;  // rank << 9
-    // lp[d-1][r+2] (past the row end when r+2 >= K: then unused)
-    const float sib_next =
-        *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sh.lp) +
-                                        rdlane(rowoff, d - 1) + (rf >> 7));
-    // sibling
-    uint32_t ks_lo = xl + 512u;
-    if (xss == kNone) ks_lo = kNone;
-    const uint64_t ks = key64(xss, ks_lo);
-    // child (lane d of the all-lane sums)
     const float s = __uint_as_float(xh);
-    const uint32_t cs = rdlane(__float_as_uint(s + tb0), dc);
-    const uint32_t css = SIB ? rdlane(__float_as_uint(s + tb1), dc) : kNone;
+    // sibling: lp[d-1][r+1] is element r+1 of lane d-1 (the index is clamped
+    // when rank r+1 does not exist: the value is then unused)
+    uint64_t ks = kEmpty;
+    if (SIB && rf + 512u < rank_lim) {
+      const float lsib = rdlane_f(tbl[min((int)(rf >> 9) + 1, 31)], d - 1);
+      ks = key64(__float_as_uint(__uint_as_float(xps) + lsib), xl + 512u);
+    }
+    // child: lane d of the all-lane sums s + lp[.][0]
+    const uint32_t cs = rdlane(__float_as_uint(s + tbl[0]), dc);
     const uint64_t kc = d < L ? key64(cs, ((xl & 0xFE000000u) + 0x02000000u) | ((uint32_t)n << 14))
                               : kEmpty;
     const bool sf = ks < kc;
     uint64_t c1 = sf ? ks : kc, c2 = sf ? kc : ks;
     const uint32_t ps1 = sf ? xps : xh, ps2 = sf ? xh : xps;
-    const uint32_t sss = (SIB && rf + 1024u < rank_lim)
-                             ? __float_as_uint(__uint_as_float(xps) + sib_next) : kNone;
-    const uint32_t ss1 = sf ? sss : css, ss2 = sf ? css : sss;
 
     if constexpr (OVER) {
       const bool in1 = c1 < omin, in2 = c2 < omin;
@@ -216,7 +210,6 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
     Hh = pick(slh, Hh, srh, (uint32_t)(c1 >> 32), (uint32_t)(c2 >> 32));
     Hl = pick(sll, Hl, srl, (uint32_t)c1, (uint32_t)c2);
     Hps = pick(dpp_zero<kShl1>(Hps), Hps, dpp_zero<kShr1>(Hps), ps1, ps2);
-    Hss = pick(dpp_zero<kShl1>(Hss), Hss, dpp_zero<kShr1>(Hss), ss1, ss2);
   };
 
   if (N > 64) {
@@ -236,14 +229,7 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
         Hh = (uint32_t)(k >> 32);
         Hl = (uint32_t)k;
         Hps = 0u;
-        Hss = kNone;
-        if (lane < take) {
-          const int d = (int)(Hl >> 25), p = (int)((Hl >> 14) & 0x7FFu);
-          const int r = (int)((Hl >> 9) & 31u);
-          const float ps = __uint_as_float((uint32_t)(sh.nkey[p] >> 32));
-          Hps = __float_as_uint(ps);
-          if (r + 1 < K) Hss = __float_as_uint(ps + sh.lp[(d - 1) * K + r + 1]);
-        }
+        if (lane < take) Hps = (uint32_t)(sh.nkey[(Hl >> 14) & 0x7FFu] >> 32);  // parent's score
         for (int i = take + lane; i < nover; i += 64) sh.over[i - take] = sh.over[i];
         nover -= take;
         omin = nover > 0 ? sh.over[0] : kEmpty;
@@ -277,24 +263,30 @@ __global__ __launch_bounds__(kBlock) void k_tree(TreeArgs a) {
   // Tables of the row stage [BDDT §3, §4.3]: candidate words (staged with
   // the key in the lp slot and the id word in the tok slot), row maxima and
   // the fixed-point partial sums of every row.
-  for (int i = tid; i < LK; i += kBlock) {
-    const uint64_t wd = a.row_cand[r0 * K + i];
-    sh.tok[i] = (int32_t)(uint32_t)wd;
-    sh.lp[i] = __uint_as_float((uint32_t)(wd >> 32));
-  }
-  for (int i = tid; i < L * S; i += kBlock) sh.over[i] = a.row_sum[r0 * S + i];
-  if (tid < L) sh.rmax[tid] = a.row_max[r0 + tid];
-  if (wid == 1 && a.status) {  // L <= 64 row flags, one per lane, OR-reduced
-    int f = lane < L ? a.row_flags[r0 + lane] : 0;
+  if (wid == 0) {
+    // lane d < L: row d's maximum and the log of its normaliser, the sum of
+    // its S <= 32 fixed-point partial sums (all requested at once)
+    const float m = lane < L ? a.row_max[r0 + lane] : -INFINITY;
+    uint64_t part[32];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, 64);
-    if (lane == 0) a.status[b] = f;
-  }
-  __syncthreads();
-  if (tid < L) {  // log of the row's normaliser
+    for (int j = 0; j < 32; ++j) part[j] = (lane < L && j < S) ? a.row_sum[(r0 + lane) * S + j] : 0ull;
     uint64_t sum = 0;
-    for (int j = 0; j < S; ++j) sum += sh.over[tid * S + j];
-    sh.rlse[tid] = sh.rmax[tid] == -INFINITY ? INFINITY : lse_from_fixed(sum);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sum += part[j];
+    if (lane < L) {
+      sh.rmax[lane] = m;
+      sh.rlse[lane] = m == -INFINITY ? INFINITY : lse_from_fixed(sum);
+    }
+  } else {
+    for (int i = tid - 64; i < LK; i += kBlock - 64) {
+      const uint64_t wd = a.row_cand[r0 * K + i];
+      sh.tok[i] = (int32_t)(uint32_t)wd;
+      sh.lp[i] = __uint_as_float((uint32_t)(wd >> 32));
+    }
+    if (wid == 1 && a.status) {  // L <= 64 row flags, one per lane, OR-reduced
+      const uint32_t f = wave_or_dpp(lane < L ? (uint32_t)a.row_flags[r0 + lane] : 0u);
+      if (lane == 0) a.status[b] = (int32_t)f;
+    }
   }
   __syncthreads();
   // log-probabilities: lp = (x - m) - lse, or at temperature 0 the argmax
