@@ -514,9 +514,12 @@ __global__ __launch_bounds__(BLOCK) void k_rows_sum(BuildArgs a, RowPlan pl) {
     if (wid == 0) {
       // threshold T: the K-th largest of the first qf words of every chunk
       // (S * qf >= K distinct words, so at least K words are >= T); lane l
-      // holds the l-th of them and counts the larger ones by broadcasts
+      // holds the l-th of them and counts the larger ones by broadcasts.
+      // The chunk maxima and flags are requested together with the words.
       const int qf = (K + S - 1) / S, n1 = S * qf;  // n1 < K + S <= 64
       const uint64_t f = lane < n1 ? pc[(lane / qf) * K + lane % qf] : 0ull;
+      const float pmax = lane < S ? a.part_max[q0 + lane] : -INFINITY;
+      const uint32_t pfl = lane < S ? (uint32_t)a.part_flags[q0 + lane] : 0u;
       const uint32_t fh = (uint32_t)(f >> 32), flo = (uint32_t)f;
       int rank = 0;
       for (int j = 0; j < n1; ++j) {
@@ -531,8 +534,8 @@ __global__ __launch_bounds__(BLOCK) void k_rows_sum(BuildArgs a, RowPlan pl) {
         T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)fh, l) << 32) |
             (uint32_t)__builtin_amdgcn_readlane((int)flo, l);
       }
-      const float m = wave_max_dpp(lane < S ? a.part_max[q0 + lane] : -INFINITY);
-      const uint32_t fl = wave_or_dpp(lane < S ? (uint32_t)a.part_flags[q0 + lane] : 0u);
+      const float m = wave_max_dpp(pmax);
+      const uint32_t fl = wave_or_dpp(pfl);
       if (lane == 0) {
         s_T = T;
         a.row_max[r] = m;
@@ -573,8 +576,10 @@ __global__ __launch_bounds__(BLOCK) void k_rows_sum(BuildArgs a, RowPlan pl) {
 
   // row maximum and status bits over the S chunks (S <= 64: one load per lane)
   const int q0 = r * pl.S;
-  const float m = wave_max_dpp(lane < pl.S ? a.part_max[q0 + lane] : -INFINITY);
-  const uint32_t fl = wave_or_dpp(lane < pl.S ? (uint32_t)a.part_flags[q0 + lane] : 0u);
+  const float pmax = lane < pl.S ? a.part_max[q0 + lane] : -INFINITY;
+  const uint32_t pfl = lane < pl.S ? (uint32_t)a.part_flags[q0 + lane] : 0u;
+  const float m = wave_max_dpp(pmax);
+  const uint32_t fl = wave_or_dpp(pfl);
 
   double acc = 0.0;
   const bool finite_m = m != -INFINITY;
@@ -684,8 +689,9 @@ hipError_t launch_dt(const BuildArgs& a, RowPlan pl, hipStream_t st) {
 }  // namespace
 
 // Rows are split when there are too few of them to give the chip ~512
-// workgroups: S chunks of cv >= 128 vectors each (so no chunk is empty),
-// S <= 32 and S * K <= 512 (the merge holds all S * K words in LDS).
+// workgroups: S chunks of cv >= 256 vectors each (a vector per thread or
+// more, and no chunk empty), S <= 32 and S * K <= 512 (the merge holds all
+// S * K words in LDS).
 RowPlan plan_rows(int batch, int L, int V, int K, int esize, bool vec_ok) {
   RowPlan pl{1, 0, vec_ok};
   const int rows = batch * L;
@@ -693,7 +699,7 @@ RowPlan plan_rows(int batch, int L, int V, int K, int esize, bool vec_ok) {
   if (!vec_ok || rows >= 256) return pl;
   int S = std::min(32, 512 / K);
   S = std::min(S, (512 + rows - 1) / rows);
-  S = std::min(S, nvec / 128);
+  S = std::min(S, nvec / 256);
   if (S <= 1) return pl;
   pl.S = S;
   pl.cv = (nvec + S - 1) / S;

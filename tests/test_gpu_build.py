@@ -53,6 +53,18 @@ def test_build_matches_oracle(B, L, V, K, N, dtype, tau):
     assert_same_build(g, o)
 
 
+@pytest.mark.parametrize("B,L,V,K,N", [(1, 16, 32000, 32, 200), (1, 2, 151936, 32, 100),
+                                       (1, 4, 9000, 24, 60)])
+def test_build_split_rows_fewer_chunks_than_K(B, L, V, K, N):
+    """Split rows where S < K chunks: the merge threshold is the K-th largest
+    of the first ceil(K/S) words of every chunk."""
+    x = _logits(B, L, V, seed=V + K, sigma=1.0, boost=0.0)
+    note("build split S<K B=%d L=%d V=%d K=%d N=%d" % (B, L, V, K, N))
+    g, _ = gpu_build(x, list(range(B)), K, N, 1.0)
+    o = oracle.build_tree(x, list(range(B)), K, N, 1.0)
+    assert_same_build(g, o)
+
+
 def test_build_adversarial_rows():
     B, L, V, K, N = 2, 6, 5000, 16, 120
     x = _logits(B, L, V, seed=5, dtype=torch.float32)
