@@ -50,8 +50,14 @@ def lib():
         L.oracle_row_topk.restype = ctypes.c_int
         L.oracle_tree.restype = ctypes.c_int
         for name in ("oracle_mask", "oracle_build", "oracle_attn_rows",
-                     "oracle_argmax_rows", "oracle_walk", "oracle_accept"):
+                     "oracle_argmax_rows", "oracle_walk", "oracle_accept",
+                     "oracle_philox4x32_10", "oracle_accept_sample"):
             getattr(L, name).restype = None
+        L.oracle_sample_row.restype = ctypes.c_int
+        L.oracle_sample_row.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int]
+        L.oracle_accept_sample.argtypes = [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 3 + \
+            [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64] + [ctypes.c_void_p] * 5
         _lib = L
     return _lib
 
@@ -219,4 +225,40 @@ def accept(target_logits, target_ids, tokens, parents, num_nodes, L: int):
     lib().oracle_accept(_p(raw), dt, _p(ids), _p(tk), _p(pa), _p(nn), B, T, V, L,
                         _p(out["accepted"]), _p(out["accepted_nodes"]), _p(out["accept_len"]),
                         _p(out["bonus"]), _p(out["target_argmax"]))
+    return out
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32 with 10 rounds: four 32-bit counter words, two key words."""
+    c = np.asarray(counter, dtype=np.uint32)
+    k = np.asarray(key, dtype=np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().oracle_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def sample_row(row, tau: float, seed: int, offset: int, b: int = 0, i: int = 0) -> int:
+    """The sampled target token of one logit row (temperature tau > 0)."""
+    raw, dt = as_raw(row)
+    raw = np.ascontiguousarray(raw.reshape(-1))
+    return int(lib().oracle_sample_row(_p(raw), dt, raw.size, float(tau), int(seed), int(offset),
+                                       int(b), int(i)))
+
+
+def accept_sample(target_logits, tokens, parents, num_nodes, L: int, tau: float, seed: int,
+                  offset: int):
+    """Acceptance at target temperature tau > 0: sampled tokens, then the walk."""
+    tk = _i32(tokens)
+    B, T = tk.shape
+    pa = _i32(parents)
+    nn = _i32(num_nodes)
+    raw, dt = as_raw(target_logits)
+    V = raw.shape[-1]
+    out = dict(accepted=np.zeros((B, L), np.int32), accepted_nodes=np.zeros((B, L), np.int32),
+               accept_len=np.zeros(B, np.int32), bonus=np.zeros(B, np.int32),
+               target_tokens=np.zeros((B, T), np.int32))
+    lib().oracle_accept_sample(_p(raw), dt, _p(tk), _p(pa), _p(nn), B, T, V, L, float(tau),
+                               int(seed), int(offset), _p(out["accepted"]),
+                               _p(out["accepted_nodes"]), _p(out["accept_len"]), _p(out["bonus"]),
+                               _p(out["target_tokens"]))
     return out

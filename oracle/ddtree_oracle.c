@@ -521,3 +521,110 @@ void oracle_accept(const void *target_logits, int dtype, const int32_t *target_i
     }
     free(tgt);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Next step: acceptance at target temperature tau_t > 0         [BDDT §4.1] */
+/*                                                                          */
+/* The walk is the same; the target's token after node i is a sample of     */
+/* softmax(logits_i / tau_t) instead of its argmax. The sample is exact and */
+/* reproducible: the weights are the fixed-point terms u_v of the numerics  */
+/* spec (x_v = fp32(logit_v * fp32(1/tau_t)), NaN / +inf -> -inf, m = max,  */
+/* u_v = rint(2^44 E(x_v - m)), S = sum u_v), a 64-bit uniform r comes from */
+/* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as  */
+/* easy as 1, 2, 3", SC 2011) with key (seed_lo, seed_hi) and counter       */
+/* (i, b, offset_lo, offset_hi), r = word1 * 2^32 + word0, and the token is */
+/* the first v whose running sum of u exceeds theta = floor(r * S / 2^64).  */
+/* Token v is then drawn with probability u_v / S. A row without a finite   */
+/* value (S = 0) gives token 0.                                             */
+/* ------------------------------------------------------------------------ */
+static void philox_round(uint32_t c[4], const uint32_t k[2])
+{
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k[0];
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k[1];
+    const uint32_t n3 = (uint32_t)p0;
+    c[0] = n0;
+    c[1] = n1;
+    c[2] = n2;
+    c[3] = n3;
+}
+
+/* Philox4x32 with 10 rounds: the key is bumped by the Weyl constants between
+ * rounds. */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k[2] = {key[0], key[1]};
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k[0] += 0x9E3779B9u;
+            k[1] += 0xBB67AE85u;
+        }
+        philox_round(c, k);
+    }
+    for (int j = 0; j < 4; ++j)
+        out[j] = c[j];
+}
+
+/* The sampled token of one row (see above). */
+int oracle_sample_row(const void *row, int dtype, int V, float tau, uint64_t seed, uint64_t offset,
+                      int b, int i)
+{
+    const float inv_tau = 1.0f / tau;
+    int flags = 0;
+    float m = -INFINITY;
+    for (int v = 0; v < V; ++v) {
+        float x = sanitized(row, dtype, (size_t)v, tau, inv_tau, &flags);
+        if (x > m)
+            m = x;
+    }
+    if (m == -INFINITY)
+        return 0;
+    uint64_t S = 0;
+    for (int v = 0; v < V; ++v)
+        S += oracle_exp_fixed(sanitized(row, dtype, (size_t)v, tau, inv_tau, &flags) - m);
+    const uint32_t ctr[4] = {(uint32_t)i, (uint32_t)b, (uint32_t)offset, (uint32_t)(offset >> 32)};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    oracle_philox4x32_10(ctr, key, w);
+    const uint64_t r = ((uint64_t)w[1] << 32) | w[0];
+    const uint64_t theta = (uint64_t)(((unsigned __int128)r * S) >> 64);
+    uint64_t run = 0;
+    for (int v = 0; v < V; ++v) {
+        run += oracle_exp_fixed(sanitized(row, dtype, (size_t)v, tau, inv_tau, &flags) - m);
+        if (run > theta)
+            return v;
+    }
+    return V - 1; /* not reached: run ends at S > theta */
+}
+
+/* Sampled target tokens and the walk for a batch; target_tokens [batch, T]
+ * gets -1 for rows at or beyond num_nodes[b]. */
+void oracle_accept_sample(const void *target_logits, int dtype, const int32_t *tokens,
+                          const int32_t *parents, const int32_t *num_nodes, int batch, int T, int V,
+                          int L, float tau, uint64_t seed, uint64_t offset, int32_t *accepted,
+                          int32_t *accepted_nodes, int32_t *accept_len, int32_t *bonus,
+                          int32_t *target_tokens)
+{
+    size_t elem = (dtype == ODT_BF16) ? 2 : 4;
+    int32_t *tgt = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
+    for (int b = 0; b < batch; ++b) {
+        for (int i = 0; i < T; ++i) {
+            if (i >= num_nodes[b]) {
+                tgt[i] = -1;
+            } else {
+                const char *row =
+                    (const char *)target_logits + ((size_t)b * T + i) * (size_t)V * elem;
+                tgt[i] = oracle_sample_row(row, dtype, V, tau, seed, offset, b, i);
+            }
+            if (target_tokens)
+                target_tokens[(size_t)b * T + i] = tgt[i];
+        }
+        size_t o = (size_t)b * T;
+        oracle_walk(tokens + o, parents + o, num_nodes[b], tgt, L, accepted + (size_t)b * L,
+                    accepted_nodes + (size_t)b * L, accept_len + b, bonus + b);
+    }
+    free(tgt);
+}
