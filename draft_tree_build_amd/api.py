@@ -56,6 +56,10 @@ def lib():
                                          i32, i64, f32, vp, vp, sz, vp]
         L.ddtree_accept_workspace_size.restype = sz
         L.ddtree_accept_workspace_size.argtypes = [i32, i32]
+        L.ddtree_accept_sample.restype = i32
+        L.ddtree_accept_sample.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, f32,
+                                           ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp, vp,
+                                           vp, sz, vp]
         L.ddtree_accept.restype = i32
         L.ddtree_accept.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp,
                                     vp, vp, sz, vp]
@@ -174,6 +178,24 @@ def ddtree_accept(target_logits: Optional[torch.Tensor], target_ids: Optional[to
         _ptr(target_argmax), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream, tokens.device))
     _check("ddtree_accept", code)
+
+
+def ddtree_accept_sample(target_logits: torch.Tensor, tokens: torch.Tensor,
+                         parents: torch.Tensor, num_nodes: torch.Tensor, L: int,
+                         temperature: float, seed: int, offset: int, accepted: torch.Tensor,
+                         accepted_nodes: Optional[torch.Tensor], accept_len: torch.Tensor,
+                         bonus: torch.Tensor, target_tokens: Optional[torch.Tensor],
+                         workspace: Optional[torch.Tensor], stream=None) -> None:
+    batch, T = tokens.shape
+    V = target_logits.shape[-1]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    code = lib().ddtree_accept_sample(
+        _ptr(target_logits), _dtype_code(target_logits), _ptr(tokens), _ptr(parents),
+        _ptr(num_nodes), batch, T, V, L, float(temperature), int(seed) & (2**64 - 1),
+        int(offset) & (2**64 - 1), _ptr(accepted), _ptr(accepted_nodes), _ptr(accept_len),
+        _ptr(bonus), _ptr(target_tokens), _ptr(workspace), nbytes,
+        _stream(stream, tokens.device))
+    _check("ddtree_accept_sample", code)
 
 
 # ----------------------------------------------------------------- convenience

@@ -179,4 +179,39 @@ int ddtree_accept(const void* target_logits, ddtree_dtype dt, const int32_t* tar
   return hip_status(launch_accept(a, w, static_cast<hipStream_t>(stream)));
 }
 
+int ddtree_accept_sample(const void* target_logits, ddtree_dtype dt, const int32_t* tokens,
+                         const int32_t* parents, const int32_t* num_nodes, int batch, int T, int V,
+                         int L, float temperature, uint64_t seed, uint64_t offset,
+                         int32_t* accepted, int32_t* accepted_nodes, int32_t* accept_len,
+                         int32_t* bonus, int32_t* target_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!target_logits || !tokens || !parents || !num_nodes || !accepted || !accept_len || !bonus)
+    return DDTREE_ERR_ARG;
+  if (batch < 1 || T < 1 || L < 1 || V < 1) return DDTREE_ERR_ARG;
+  if (!(temperature > 0.0f) || isinf(temperature)) return DDTREE_ERR_ARG;
+  if (!dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
+  if (T > DDTREE_MAX_N + 1 || L > DDTREE_MAX_L) return DDTREE_ERR_UNSUPPORTED;
+  if ((long long)batch * T > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  if (!target_tokens && (!workspace || workspace_bytes < accept_workspace_bytes(batch, T)))
+    return DDTREE_ERR_WORKSPACE;
+  AcceptArgs a{};
+  a.target_logits = target_logits;
+  a.dtype = dt;
+  a.tokens = tokens;
+  a.parents = parents;
+  a.num_nodes = num_nodes;
+  a.batch = batch;
+  a.T = T;
+  a.V = V;
+  a.L = L;
+  a.accepted = accepted;
+  a.accepted_nodes = accepted_nodes;
+  a.accept_len = accept_len;
+  a.bonus = bonus;
+  int32_t* tgt = target_tokens ? target_tokens : static_cast<int32_t*>(workspace);
+  const float inv_tau = 1.0f / temperature;
+  return hip_status(launch_accept_sample(a, inv_tau, seed, offset, tgt,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -115,6 +115,9 @@ int accept_splits(int batch, int T);
 size_t accept_workspace_bytes(int batch, int T);
 AcceptWork accept_carve(void* ws, int batch, int T);
 hipError_t launch_accept(const AcceptArgs& a, const AcceptWork& w, hipStream_t stream);
+// tgt: [batch, T] sampled tokens (-1 past num_nodes), then the walk from them
+hipError_t launch_accept_sample(const AcceptArgs& a, float inv_tau, uint64_t seed, uint64_t offset,
+                                int32_t* tgt, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -231,6 +231,145 @@ __global__ __launch_bounds__(BLOCK) void k_walk(AcceptArgs a, int S2, const floa
   }
 }
 
+// ---------------------------------------------------------------------------
+// Acceptance at target temperature tau > 0 [BDDT §4.1]: the target's token
+// after node i is a sample of softmax(logits_i / tau). The weights are the
+// fixed-point terms of the numerics spec, u_v = rint(2^44 E(x_v - m)) with
+// x_v = fp32(logit_v * inv_tau) (NaN, +inf -> -inf) and m = max_v x_v; the
+// uniform r (64 bits) is Philox4x32-10 (Salmon et al., SC 2011) with key
+// (seed_lo, seed_hi) and counter (i, b, offset_lo, offset_hi), r = word1 *
+// 2^32 + word0; the token is the first v whose running sum of u exceeds
+// theta = floor(r * S / 2^64), S = sum_v u_v. A row with no finite value
+// gives token 0. Integer sums make the draw exact and order-free.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// Inclusive prefix sum of a uint64 over the 64 lanes of a wave.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_up((unsigned int)v, (unsigned int)o, 64);
+    const uint32_t hi = __shfl_up((unsigned int)(v >> 32), (unsigned int)o, 64);
+    if (lane >= o) v += ((uint64_t)hi << 32) | lo;
+  }
+  return v;
+}
+
+// Element e of a row (any alignment), as the sampling value x (sanitised).
+template <typename IN_T>
+__device__ __forceinline__ float sample_x(const IN_T* row, int e, float inv_tau) {
+  float x;
+  if constexpr (sizeof(IN_T) == 2) x = bf16_to_float(reinterpret_cast<const uint16_t*>(row)[e]);
+  else x = reinterpret_cast<const float*>(row)[e];
+  x = x * inv_tau;
+  return ((x != x) || (x == INFINITY)) ? -INFINITY : x;
+}
+
+// One workgroup of 256 threads per (request, node) row. Thread t owns the
+// contiguous elements [t*seg, (t+1)*seg) so that the block's exclusive scan
+// of the thread sums is a running sum in token order; the owner of theta
+// hands its segment to wave 0 (64 sub-segments, one wave scan) and the lane
+// that holds theta finds the token.
+template <typename IN_T>
+__global__ __launch_bounds__(256) void k_sample(AcceptArgs a, float inv_tau, uint64_t seed,
+                                                uint64_t offset, int32_t* tgt) {
+  __shared__ float s_m[4];
+  __shared__ uint64_t s_w[4];
+  __shared__ uint64_t s_theta;
+  __shared__ int s_owner;
+  __shared__ uint64_t s_base;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int T = a.T, V = a.V;
+  const int rowi = blockIdx.x;
+  const int b = rowi / T, i = rowi - b * T;
+  if (i >= min(a.num_nodes[b], T)) {
+    if (tid == 0) tgt[rowi] = -1;
+    return;
+  }
+  const IN_T* row = static_cast<const IN_T*>(a.target_logits) + (size_t)rowi * V;
+  // ---- maximum (strided, coalesced)
+  float tmax = -INFINITY;
+  for (int e = tid; e < V; e += 256) tmax = fmaxf(tmax, sample_x(row, e, inv_tau));
+  const float wm = wave_max_dpp(tmax);
+  if (lane == 0) s_m[wid] = wm;
+  if (tid == 0) s_owner = -1;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  if (m == -INFINITY) {  // no finite value: token 0
+    if (tid == 0) tgt[rowi] = 0;
+    return;
+  }
+  // ---- weights of this thread's contiguous segment and their block scan
+  const int seg = (V + 255) / 256;
+  const int e0 = min(tid * seg, V), e1 = min(e0 + seg, V);
+  uint64_t mine = 0;
+  for (int e = e0; e < e1; ++e) mine += (uint64_t)exp_fixed(sample_x(row, e, inv_tau) - m);
+  const uint64_t incl = wave_incl_scan_u64(mine, lane);
+  if (lane == 63) s_w[wid] = incl;
+  __syncthreads();
+  uint64_t before = 0, S = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wid) before += s_w[w];
+    S += s_w[w];
+  }
+  const uint64_t excl = before + incl - mine;
+  if (tid == 0) {
+    uint32_t c[4] = {(uint32_t)i, (uint32_t)b, (uint32_t)offset, (uint32_t)(offset >> 32)};
+    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const uint64_t r = ((uint64_t)c[1] << 32) | c[0];
+    s_theta = __umul64hi(r, S);
+  }
+  __syncthreads();
+  const uint64_t theta = s_theta;
+  if (excl <= theta && theta < excl + mine) {
+    s_owner = tid;
+    s_base = excl;
+  }
+  __syncthreads();
+  if (wid != 0) return;
+  // ---- wave 0: the owner's segment in 64 contiguous pieces (exactly one
+  // thread owns theta since 0 <= theta < S; the clamp only keeps indexes in
+  // the row)
+  const int own = max(s_owner, 0);
+  const int f0 = min(own * seg, V), f1 = min(f0 + seg, V);
+  const int sub = (f1 - f0 + 63) / 64;
+  const int g0 = min(f0 + lane * sub, f1), g1 = min(g0 + sub, f1);
+  uint64_t part = 0;
+  for (int e = g0; e < g1; ++e) part += (uint64_t)exp_fixed(sample_x(row, e, inv_tau) - m);
+  const uint64_t pincl = wave_incl_scan_u64(part, lane);
+  uint64_t run = s_base + pincl - part;
+  int tok = -1;
+  if (run <= theta && theta < run + part) {
+    for (int e = g0; e < g1; ++e) {
+      run += (uint64_t)exp_fixed(sample_x(row, e, inv_tau) - m);
+      if (run > theta) {
+        tok = e;
+        break;
+      }
+    }
+  }
+  const uint64_t found = __ballot(tok >= 0);
+  const int first = found ? (int)__builtin_ctzll(found) : 0;
+  const int t = __builtin_amdgcn_readlane(tok, first);
+  if (lane == 0) tgt[rowi] = max(t, 0);
+}
+
 template <typename IN_T>
 hipError_t launch_logits(const AcceptArgs& a, const AcceptWork& w, hipStream_t st) {
   const bool vec = (reinterpret_cast<uintptr_t>(a.target_logits) % 16 == 0) &&
@@ -273,6 +412,26 @@ AcceptWork accept_carve(void* ws, int batch, int T) {
   w.pv = reinterpret_cast<float*>(ws);
   w.pidx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(parts * 4, 256));
   return w;
+}
+
+hipError_t launch_accept_sample(const AcceptArgs& a, float inv_tau, uint64_t seed,
+                                uint64_t offset, int32_t* tgt, hipStream_t st) {
+  dim3 grid(a.batch * a.T);
+  if (a.dtype == 0)
+    hipLaunchKernelGGL(k_sample<uint16_t>, grid, dim3(256), 0, st, a, inv_tau, seed, offset, tgt);
+  else
+    hipLaunchKernelGGL(k_sample<float>, grid, dim3(256), 0, st, a, inv_tau, seed, offset, tgt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AcceptArgs w = a;
+  w.target_logits = nullptr;
+  w.target_ids = tgt;
+  w.target_argmax = nullptr;
+  if (a.T <= 256)
+    hipLaunchKernelGGL((k_walk<true, 256>), dim3(a.batch), dim3(256), 0, st, w, 0, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL((k_walk<true, 1024>), dim3(a.batch), dim3(1024), 0, st, w, 0, nullptr, nullptr);
+  return hipGetLastError();
 }
 
 hipError_t launch_accept(const AcceptArgs& a, const AcceptWork& w, hipStream_t st) {

@@ -177,6 +177,44 @@ int ddtree_accept(const void *target_logits, ddtree_dtype dt, const int32_t *tar
                   int32_t *accept_len, int32_t *bonus, int32_t *target_argmax, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/*
+ * ddtree_accept_sample -- acceptance walk at target temperature > 0.
+ *                                                                [BDDT §4.1]
+ * The target's token after node i of request b is a sample of
+ * softmax(target_logits[b, i, :] / temperature); the walk is that of
+ * ddtree_accept with these tokens in place of the arg-max. The draw is exact
+ * and reproducible: with x_v = fp32(logit_v * fp32(1 / temperature)) (NaN
+ * and +inf count as -inf), m = max_v x_v and the integer weights
+ * u_v = rint(2^44 E(x_v - m)) of the fixed-point exponential that
+ * ddtree_build uses, the token is the first v whose running sum of u exceeds
+ * floor(r * S / 2^64), S = sum_v u_v, where r = word1 * 2^32 + word0 of
+ * Philox4x32-10 (Salmon et al., SC 2011) with key (seed mod 2^32,
+ * seed / 2^32) and counter (i, b, offset mod 2^32, offset / 2^32). A row with
+ * no finite value gives token 0. Callers advance offset once per round.
+ *
+ *   target_logits   [batch, T, V] dt                      in
+ *   tokens, parents [batch, T] int32, num_nodes [batch]   in (ddtree_build output)
+ *   temperature     > 0, finite (else DDTREE_ERR_ARG)
+ *   seed, offset    Philox key and the high half of its counter
+ *   accepted        [batch, L] int32                      out: accepted tokens, -1 padded
+ *   accepted_nodes  [batch, L] int32 or NULL              out: their node indices
+ *   accept_len      [batch] int32                         out
+ *   bonus           [batch] int32                         out: the sample at the last
+ *                   accepted node
+ *   target_tokens   [batch, T] int32 or NULL              out: the sampled token per
+ *                   node (-1 for rows >= num_nodes[b])
+ *   workspace       >= ddtree_accept_workspace_size(batch, T) bytes when
+ *                   target_tokens is NULL (holds the sampled tokens); else
+ *                   unused and may be NULL
+ * Limits: T <= 1025, 1 <= L <= 64, 1 <= V <= 2^31 - 1.
+ */
+int ddtree_accept_sample(const void *target_logits, ddtree_dtype dt, const int32_t *tokens,
+                         const int32_t *parents, const int32_t *num_nodes, int batch, int T, int V,
+                         int L, float temperature, uint64_t seed, uint64_t offset,
+                         int32_t *accepted, int32_t *accepted_nodes, int32_t *accept_len,
+                         int32_t *bonus, int32_t *target_tokens, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = ctypes.CDLL(api.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -119,6 +119,28 @@ def _accept(**kw):
 def test_accept_rejects(kw, code):
     _no_gpu()
     assert _accept(**kw) == code
+
+
+def _sample(**kw):
+    a = dict(tl=P, dt=0, tok=P, par=P, nn=P, batch=1, T=9, V=64, L=4, temp=1.0, seed=1, off=0,
+             acc=P, accn=N0, alen=P, bonus=P, targ=N0, ws=P, wsb=1 << 16)
+    a.update(kw)
+    return api.lib().ddtree_accept_sample(a["tl"], a["dt"], a["tok"], a["par"], a["nn"],
+                                          a["batch"], a["T"], a["V"], a["L"], a["temp"],
+                                          a["seed"], a["off"], a["acc"], a["accn"], a["alen"],
+                                          a["bonus"], a["targ"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tl=N0), ERR_ARG), (dict(par=N0), ERR_ARG), (dict(acc=N0), ERR_ARG), (dict(V=0), ERR_ARG),
+    (dict(T=0), ERR_ARG), (dict(L=0), ERR_ARG), (dict(temp=0.0), ERR_ARG),
+    (dict(temp=-0.5), ERR_ARG), (dict(temp=float("inf")), ERR_ARG),
+    (dict(temp=float("nan")), ERR_ARG), (dict(dt=5), ERR_UNSUP), (dict(L=65), ERR_UNSUP),
+    (dict(T=1026), ERR_UNSUP), (dict(ws=N0), ERR_WS), (dict(wsb=8), ERR_WS),
+])
+def test_accept_sample_rejects(kw, code):
+    _no_gpu()
+    assert _sample(**kw) == code
 
 
 def test_mask_rejects():
