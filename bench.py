@@ -4,8 +4,10 @@
 
 A step is one whole round on one batch of synthetic input: ddtree_build
 (log-softmax + top-K + best-first tree + mask), ddtree_verify_attn (tree
-attention over the prefix KV) and ddtree_accept (target argmax + walk), all
-enqueued on the current HIP stream. Inputs are resident in HBM before the
+attention over the prefix KV) and ddtree_accept (target argmax + walk; with
+--target-temp T > 0, ddtree_accept_sample: a sample of the target's softmax at
+temperature T per node, then the walk), all enqueued on the current HIP
+stream. Inputs are resident in HBM before the
 timed region; several copies rotate from step to step so that a step's
 reads come from HBM rather than from the 256 MB last-level cache.
 
@@ -37,10 +39,13 @@ KERNEL_SOURCES = {
     "build": ["draft_tree_build_amd/csrc/k_build.hip", "draft_tree_build_amd/csrc/k_tree.hip"],
     "verify": ["draft_tree_build_amd/csrc/k_attn.hip"],
     "accept": ["draft_tree_build_amd/csrc/k_accept.hip"],
+    "accept_sample": ["draft_tree_build_amd/csrc/k_accept.hip"],
 }
 KERNEL_NAMES = {"build": "ddtree_build: k_rows (+ k_rows_sum for split rows), k_tree",
                 "verify": "ddtree_verify_attn: k_attn_mfma (+ k_attn_combine for split keys)",
-                "accept": "ddtree_accept: k_argmax, k_walk"}
+                "accept": "ddtree_accept: k_argmax, k_walk",
+                "accept_sample": "ddtree_accept_sample: k_sample, k_walk"}
+SAMPLE_SEED = 0x5EED
 
 
 def log(msg):
@@ -91,7 +96,7 @@ def graphs_off(args):
     return not args.graphs
 
 
-def cpu_baseline(w, inputs, nodes_per_step, budget_s):
+def cpu_baseline(w, inputs, nodes_per_step, budget_s, target_temp):
     """The oracle, single-threaded, on whole rounds of the same workload."""
     import numpy as np
     import oracle
@@ -103,14 +108,21 @@ def cpu_baseline(w, inputs, nodes_per_step, budget_s):
         tree = oracle.build_tree(x, roots, w.K, w.N, tau)
         oracle.attn_rows(q, k, v, offs, P, tree["num_nodes"], tree["mask"], w.T, w.Hq, w.Hkv, w.D,
                          1.0 / math.sqrt(w.D), sel)
-        oracle.accept(tl, None, tree["tokens"], tree["parents"], tree["num_nodes"], w.L)
+        if target_temp > 0:
+            oracle.accept_sample(tl, tree["tokens"], tree["parents"], tree["num_nodes"], w.L,
+                                 target_temp, SAMPLE_SEED, rounds)
+        else:
+            oracle.accept(tl, None, tree["tokens"], tree["parents"], tree["num_nodes"], w.L)
         rounds += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     return dict(value=nodes_per_step * rounds / el, unit="nodes/s", cores=1, kind="oracle",
-                sample="%d whole round(s) of %s (build, attention of all %d query rows, accept), "
-                       "single thread, %.1f s" % (rounds, w.name, len(sel), el))
+                sample="%d whole round(s) of %s (build, attention of all %d query rows, %s), "
+                       "single thread, %.1f s" % (rounds, w.name, len(sel),
+                                                  "sampled accept at target temperature %g"
+                                                  % target_temp if target_temp > 0 else "accept",
+                                                  el))
 
 
 def main():
@@ -125,6 +137,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", dest="graphs", action="store_false",
                     help="launch the ABI calls eagerly instead of replaying captured HIP graphs")
+    ap.add_argument("--target-temp", type=float, default=0.0,
+                    help="target temperature of the acceptance (0: greedy arg-max; > 0: "
+                         "ddtree_accept_sample)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -168,8 +183,10 @@ def main():
     stages = (
         lambda c: rnd.build(c[0], roots, tau),
         lambda c: rnd.verify(c[1], c[2], c[3], offs, P),
-        lambda c: rnd.accept(c[4]),
+        (lambda c: rnd.accept_sample(c[4], args.target_temp, SAMPLE_SEED, 0))
+        if args.target_temp > 0 else (lambda c: rnd.accept(c[4])),
     )
+    accept_kind = "accept_sample" if args.target_temp > 0 else "accept"
 
     log("warmup %d steps (eager)" % args.warmup)
     for i in range(args.warmup):
@@ -250,15 +267,17 @@ def main():
     else:
         nbytes = work[dom + "_bytes"]
         achieved, peak, unit, bound = nbytes / t_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    kname = accept_kind if dom == "accept" else dom
     roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
-                    frac=round(achieved / peak, 5), traffic=load_traffic(w.name, dom),
-                    kernel=KERNEL_NAMES[dom], stage=dom, avg_launch_us=round(stage_us[dom], 3))
+                    frac=round(achieved / peak, 5), traffic=load_traffic(w.name, kname),
+                    kernel=KERNEL_NAMES[kname], stage=kname,
+                    avg_launch_us=round(stage_us[dom], 3))
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (%.0f s budget)" % args.cpu_seconds)
         inputs = (x_cpu, roots_cpu, q_cpu, k_cpu, v_cpu, P_cpu.numpy(), offs_cpu.numpy(), tl_cpu)
-        cpu = cpu_baseline(w, inputs, nodes_per_step, args.cpu_seconds)
+        cpu = cpu_baseline(w, inputs, nodes_per_step, args.cpu_seconds, args.target_temp)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
@@ -268,7 +287,7 @@ def main():
                 "Q/K/V ~N(0,1))",
         "config": {"workload": w.name, "batch": w.batch, "L": w.L, "V": w.V, "K": w.K, "N": w.N,
                    "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                   "draft_temp": tau, "input_copies": R, "hip_graphs": bool(args.graphs),
+                   "draft_temp": tau, "target_temp": args.target_temp, "input_copies": R, "hip_graphs": bool(args.graphs),
                    "stage_event_steps": len(sampled)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": roofline,

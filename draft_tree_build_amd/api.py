@@ -250,3 +250,11 @@ class Round:
         ddtree_accept(target_logits, None, self.tokens, self.parents, self.num_nodes, self.L,
                       self.accepted, self.accepted_nodes, self.accept_len, self.bonus,
                       self.target_argmax, self.ws_accept, stream)
+
+    def accept_sample(self, target_logits, temperature: float, seed: int, offset: int,
+                      stream=None):
+        """Acceptance at target temperature > 0; the sampled token per node
+        goes to ``target_argmax`` (the per-node target token buffer)."""
+        ddtree_accept_sample(target_logits, self.tokens, self.parents, self.num_nodes, self.L,
+                             temperature, seed, offset, self.accepted, self.accepted_nodes,
+                             self.accept_len, self.bonus, self.target_argmax, None, stream)

@@ -270,29 +270,142 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
   return v;
 }
 
-// Element e of a row (any alignment), as the sampling value x (sanitised).
+// Eight consecutive row values as raw bits (bf16: four dwords, f32: eight).
 template <typename IN_T>
-__device__ __forceinline__ float sample_x(const IN_T* row, int e, float inv_tau) {
-  float x;
-  if constexpr (sizeof(IN_T) == 2) x = bf16_to_float(reinterpret_cast<const uint16_t*>(row)[e]);
-  else x = reinterpret_cast<const float*>(row)[e];
-  x = x * inv_tau;
-  return ((x != x) || (x == INFINITY)) ? -INFINITY : x;
+struct Unit8 {
+  uint32_t w[sizeof(IN_T) * 4];
+};
+
+template <typename IN_T>
+__device__ __forceinline__ void unit_load(const IN_T* row, int u, Unit8<IN_T>& r) {
+  const uint4* p = reinterpret_cast<const uint4*>(row) + (size_t)u * (sizeof(IN_T) / 2);
+#pragma unroll
+  for (int h = 0; h < (int)sizeof(IN_T) / 2; ++h) {
+    const uint4 q = p[h];
+    r.w[4 * h] = q.x;
+    r.w[4 * h + 1] = q.y;
+    r.w[4 * h + 2] = q.z;
+    r.w[4 * h + 3] = q.w;
+  }
 }
 
-// One workgroup of 256 threads per (request, node) row. Thread t owns the
-// contiguous elements [t*seg, (t+1)*seg) so that the block's exclusive scan
-// of the thread sums is a running sum in token order; the owner of theta
-// hands its segment to wave 0 (64 sub-segments, one wave scan) and the lane
-// that holds theta finds the token.
+// Rows whose start is not 16-byte aligned: element by element; -inf past the
+// row's end.
 template <typename IN_T>
-__global__ __launch_bounds__(256) void k_sample(AcceptArgs a, float inv_tau, uint64_t seed,
-                                                uint64_t offset, int32_t* tgt) {
-  __shared__ float s_m[4];
-  __shared__ uint64_t s_w[4];
-  __shared__ uint64_t s_theta;
-  __shared__ int s_owner;
-  __shared__ uint64_t s_base;
+__device__ __forceinline__ void unit_load_scalar(const IN_T* row, int u, int V, Unit8<IN_T>& r) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int e = u * 8 + k;
+    if constexpr (sizeof(IN_T) == 2) {
+      const uint32_t bits = e < V ? reinterpret_cast<const uint16_t*>(row)[e] : 0xFF80u;
+      if (k & 1) r.w[k >> 1] |= bits << 16;
+      else r.w[k >> 1] = bits;
+    } else {
+      r.w[k] = e < V ? reinterpret_cast<const uint32_t*>(row)[e] : 0xFF800000u;
+    }
+  }
+}
+
+template <typename IN_T>
+__device__ __forceinline__ void unit_fill_neg_inf(Unit8<IN_T>& r) {
+#pragma unroll
+  for (int h = 0; h < (int)sizeof(IN_T) * 4; ++h) r.w[h] = sizeof(IN_T) == 2 ? 0xFF80FF80u : 0xFF800000u;
+}
+
+// Value k of a unit as stored (bf16 widened to fp32 exactly).
+template <typename IN_T>
+__device__ __forceinline__ float unit_raw(const Unit8<IN_T>& r, int k) {
+  if constexpr (sizeof(IN_T) == 2)
+    return (k & 1) ? __uint_as_float(r.w[k >> 1] & 0xFFFF0000u) : __uint_as_float(r.w[k >> 1] << 16);
+  else
+    return __uint_as_float(r.w[k]);
+}
+
+// Value k as the sampling value x = fp32(raw * inv_tau) (TAU1: inv_tau is 1,
+// the product is the value itself); SAN: NaN and +inf ranked as -inf. Rows
+// without NaN, +inf or an overflowing product need no SAN.
+template <typename IN_T, bool TAU1, bool SAN>
+__device__ __forceinline__ float unit_x(const Unit8<IN_T>& r, int k, float inv_tau) {
+  float v = unit_raw(r, k);
+  if constexpr (!TAU1) v = v * inv_tau;
+  if constexpr (SAN) v = (v < INFINITY) ? v : -INFINITY;
+  return v;
+}
+
+// Maximum of the stored values, and whether any is NaN or +inf.
+template <typename IN_T>
+__device__ __forceinline__ float unit_max_raw(const Unit8<IN_T>& r, float acc, bool& bad) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float v = unit_raw(r, k);
+    bad |= !(v < INFINITY);
+    acc = fmaxf(acc, v);
+  }
+  return acc;
+}
+
+template <typename IN_T, bool TAU1>
+__device__ __forceinline__ float unit_max(const Unit8<IN_T>& r, float inv_tau, float acc) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc = fmaxf(acc, unit_x<IN_T, TAU1, true>(r, k, inv_tau));
+  return acc;
+}
+
+// Replaces every value whose product with inv_tau is NaN or +inf by -inf, in
+// place: afterwards the unsanitised weights are the sanitised ones.
+template <typename IN_T, bool TAU1>
+__device__ __forceinline__ void unit_sanitize(Unit8<IN_T>& r, float inv_tau) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float x = unit_raw(r, k);
+    if constexpr (!TAU1) x = x * inv_tau;
+    if (!(x < INFINITY)) {
+      if constexpr (sizeof(IN_T) == 2)
+        r.w[k >> 1] = (k & 1) ? ((r.w[k >> 1] & 0xFFFFu) | 0xFF800000u)
+                              : ((r.w[k >> 1] & 0xFFFF0000u) | 0xFF80u);
+      else
+        r.w[k] = 0xFF800000u;
+    }
+  }
+}
+
+// Sum of the unit's eight fixed-point weights (each <= 2^44: exact in fp64).
+template <typename IN_T, bool TAU1, bool SAN>
+__device__ __forceinline__ double unit_sum(const Unit8<IN_T>& r, float m, float inv_tau) {
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += exp_fixed(unit_x<IN_T, TAU1, SAN>(r, k, inv_tau) - m);
+  return s;
+}
+
+constexpr int kSampleBlock = 1024;
+constexpr int kSampleWaves = kSampleBlock / 64;
+constexpr int kSampleBatch = 4;  // units per lane per round trip when streamed
+
+// One workgroup of 1024 threads per (request, node) row; rows >= num_nodes
+// get -1. The row is cut into units of eight values; wave w owns the
+// contiguous units [64 C w, 64 C (w + 1)) and lane l of it the units
+// 64 C w + 64 j + l (j < C), so every load is a coalesced 1 KiB (bf16) per
+// wave and the token order is (wave, slot j, lane, element). CH > 0: the
+// row stays in registers (C = CH units per lane) between the maximum, the
+// sums and the search; CH == 0: it is streamed (C = chs) and read again.
+// AL: rows start 16-byte aligned and V % 8 == 0 (whole-unit vector loads).
+// TAU1: inv_tau == 1.
+// The maximum is taken over the stored values and scaled once: rounding is
+// monotone, so fp32(max raw * inv_tau) is the maximum of the products when
+// no value is NaN or +inf and that product is finite; otherwise the exact
+// maximum of the sanitised products is taken in a second pass, and the sums
+// sanitise too. The search: the wave whose range of the running sum holds
+// theta walks its slots j with one wave sum each, then the lane (inclusive
+// wave scan) and the value; sums are integers, so the result is that of a
+// scan in token order.
+template <typename IN_T, int CH, bool AL, bool TAU1>
+__global__ __launch_bounds__(kSampleBlock) void k_sample(AcceptArgs a, float inv_tau,
+                                                         uint64_t seed, uint64_t offset, int chs,
+                                                         int32_t* tgt) {
+  __shared__ float s_m[kSampleWaves], s_m2[kSampleWaves];
+  __shared__ uint32_t s_bad[kSampleWaves];
+  __shared__ uint64_t s_w[kSampleWaves];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int T = a.T, V = a.V;
   const int rowi = blockIdx.x;
@@ -302,72 +415,199 @@ __global__ __launch_bounds__(256) void k_sample(AcceptArgs a, float inv_tau, uin
     return;
   }
   const IN_T* row = static_cast<const IN_T*>(a.target_logits) + (size_t)rowi * V;
-  // ---- maximum (strided, coalesced)
-  float tmax = -INFINITY;
-  for (int e = tid; e < V; e += 256) tmax = fmaxf(tmax, sample_x(row, e, inv_tau));
-  const float wm = wave_max_dpp(tmax);
-  if (lane == 0) s_m[wid] = wm;
-  if (tid == 0) s_owner = -1;
+  const int nunit = (V + 7) >> 3;
+  const int C = CH > 0 ? CH : chs;
+  const int ubase = wid * 64 * C + lane;
+  // loads always address a unit of the row (clamped index) and are replaced
+  // by -inf past its end, so that they issue without branches
+  auto fetch = [&](int j, Unit8<IN_T>& r) {
+    const int u = j < C ? ubase + 64 * j : nunit;  // slots past C: -inf
+    const int uc = min(u, nunit - 1);
+    if constexpr (AL) unit_load(row, uc, r);
+    else unit_load_scalar(row, uc, V, r);
+    if (u >= nunit) unit_fill_neg_inf(r);
+  };
+  Unit8<IN_T> buf[CH > 0 ? CH : kSampleBatch];
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) fetch(j, buf[j]);
+  }
+  // the uniform, computed while the loads are in flight
+  uint32_t c[4] = {(uint32_t)i, (uint32_t)b, (uint32_t)offset, (uint32_t)(offset >> 32)};
+  philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint64_t r = ((uint64_t)c[1] << 32) | c[0];
+  // ---- maximum of the stored values
+  float lmax = -INFINITY;
+  bool bad = false;
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) lmax = unit_max_raw(buf[j], lmax, bad);
+  } else {
+    for (int j0 = 0; j0 < C; j0 += kSampleBatch) {
+#pragma unroll
+      for (int q = 0; q < kSampleBatch; ++q) fetch(j0 + q, buf[q]);
+#pragma unroll
+      for (int q = 0; q < kSampleBatch; ++q) lmax = unit_max_raw(buf[q], lmax, bad);
+    }
+  }
+  if constexpr (CH > 0) {
+    // keep only the packed bits live across the barrier: the values are
+    // unpacked again for the sums (fewer registers than 8 floats per unit)
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int h = 0; h < (int)sizeof(IN_T) * 4; ++h) asm volatile("" : "+v"(buf[j].w[h]));
+  }
+  const float wm = wave_max_dpp(lmax);
+  const uint64_t wbad = __ballot(bad);
+  if (lane == 0) {
+    s_m[wid] = wm;
+    s_bad[wid] = wbad != 0;
+  }
   __syncthreads();
-  const float m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float m = s_m[0];
+  uint32_t anybad = s_bad[0];
+#pragma unroll
+  for (int w = 1; w < kSampleWaves; ++w) {
+    m = fmaxf(m, s_m[w]);
+    anybad |= s_bad[w];
+  }
+  if constexpr (!TAU1) m = m * inv_tau;
+  const bool slow = anybad != 0 || !(m < INFINITY);  // block-uniform
+  if (slow) {
+    // exact maximum of the sanitised products (rows in registers are
+    // sanitised in place first, so that the sums below need no check)
+    float l2 = -INFINITY;
+    if constexpr (CH > 0) {
+      bool unused = false;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        unit_sanitize<IN_T, TAU1>(buf[j], inv_tau);
+        l2 = unit_max_raw(buf[j], l2, unused);
+      }
+      if constexpr (!TAU1) l2 = l2 * inv_tau;
+    } else {
+      for (int j0 = 0; j0 < C; j0 += kSampleBatch) {
+#pragma unroll
+        for (int q = 0; q < kSampleBatch; ++q) fetch(j0 + q, buf[q]);
+#pragma unroll
+        for (int q = 0; q < kSampleBatch; ++q) l2 = unit_max<IN_T, TAU1>(buf[q], inv_tau, l2);
+      }
+    }
+    const float w2 = wave_max_dpp(l2);
+    if (lane == 0) s_m2[wid] = w2;
+    __syncthreads();
+    m = s_m2[0];
+#pragma unroll
+    for (int w = 1; w < kSampleWaves; ++w) m = fmaxf(m, s_m2[w]);
+  }
   if (m == -INFINITY) {  // no finite value: token 0
     if (tid == 0) tgt[rowi] = 0;
     return;
   }
-  // ---- weights of this thread's contiguous segment and their block scan
-  const int seg = (V + 255) / 256;
-  const int e0 = min(tid * seg, V), e1 = min(e0 + seg, V);
-  uint64_t mine = 0;
-  for (int e = e0; e < e1; ++e) mine += (uint64_t)exp_fixed(sample_x(row, e, inv_tau) - m);
-  const uint64_t incl = wave_incl_scan_u64(mine, lane);
-  if (lane == 63) s_w[wid] = incl;
-  __syncthreads();
-  uint64_t before = 0, S = 0;
+  // ---- the weights' sums: per slot and lane (kept for the search), per
+  // thread, per wave, whole row
+  constexpr int NS = CH > 0 ? CH : 1;
+  double su[NS];
+  uint64_t tsum = 0;
+  if constexpr (CH > 0) {
+    double ts = 0.0;  // at most 8 * CH <= 256 weights of <= 2^44: exact
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wid) before += s_w[w];
-    S += s_w[w];
-  }
-  const uint64_t excl = before + incl - mine;
-  if (tid == 0) {
-    uint32_t c[4] = {(uint32_t)i, (uint32_t)b, (uint32_t)offset, (uint32_t)(offset >> 32)};
-    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
-    const uint64_t r = ((uint64_t)c[1] << 32) | c[0];
-    s_theta = __umul64hi(r, S);
-  }
-  __syncthreads();
-  const uint64_t theta = s_theta;
-  if (excl <= theta && theta < excl + mine) {
-    s_owner = tid;
-    s_base = excl;
-  }
-  __syncthreads();
-  if (wid != 0) return;
-  // ---- wave 0: the owner's segment in 64 contiguous pieces (exactly one
-  // thread owns theta since 0 <= theta < S; the clamp only keeps indexes in
-  // the row)
-  const int own = max(s_owner, 0);
-  const int f0 = min(own * seg, V), f1 = min(f0 + seg, V);
-  const int sub = (f1 - f0 + 63) / 64;
-  const int g0 = min(f0 + lane * sub, f1), g1 = min(g0 + sub, f1);
-  uint64_t part = 0;
-  for (int e = g0; e < g1; ++e) part += (uint64_t)exp_fixed(sample_x(row, e, inv_tau) - m);
-  const uint64_t pincl = wave_incl_scan_u64(part, lane);
-  uint64_t run = s_base + pincl - part;
-  int tok = -1;
-  if (run <= theta && theta < run + part) {
-    for (int e = g0; e < g1; ++e) {
-      run += (uint64_t)exp_fixed(sample_x(row, e, inv_tau) - m);
-      if (run > theta) {
-        tok = e;
-        break;
+    for (int j = 0; j < CH; ++j) {
+      su[j] = unit_sum<IN_T, TAU1, false>(buf[j], m, inv_tau);
+      ts += su[j];
+    }
+    tsum = (uint64_t)ts;
+  } else {
+    for (int j0 = 0; j0 < C; j0 += kSampleBatch) {
+#pragma unroll
+      for (int q = 0; q < kSampleBatch; ++q) fetch(j0 + q, buf[q]);
+      double ts = 0.0;
+      if (slow) {
+#pragma unroll
+        for (int q = 0; q < kSampleBatch; ++q) ts += unit_sum<IN_T, TAU1, true>(buf[q], m, inv_tau);
+      } else {
+#pragma unroll
+        for (int q = 0; q < kSampleBatch; ++q) ts += unit_sum<IN_T, TAU1, false>(buf[q], m, inv_tau);
       }
+      tsum += (uint64_t)ts;
+    }
+  }
+  const uint64_t wsum = wave_sum_u64_dpp(tsum);
+  if (lane == 0) s_w[wid] = wsum;
+  __syncthreads();
+  uint64_t S = 0, pre = 0;
+#pragma unroll
+  for (int w = 0; w < kSampleWaves; ++w) {
+    const uint64_t v = s_w[w];
+    if (w < wid) pre += v;
+    S += v;
+  }
+  const uint64_t theta = __umul64hi(r, S);
+  // exactly one wave holds theta (0 <= theta < S)
+  if (!(pre <= theta && theta < pre + wsum)) return;
+  // ---- the slot (one wave sum per slot, in order), then the lane and value;
+  // weights are recomputed sanitised (equal to the unsanitised ones when no
+  // value needs it)
+  uint64_t run = pre, sstar = 0;
+  int jstar = -1;
+  Unit8<IN_T> t;
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (jstar < 0) {
+        const uint64_t sj = (uint64_t)su[j];
+        const uint64_t tj = wave_sum_u64_dpp(sj);
+        if (theta < run + tj) {
+          jstar = j;
+          sstar = sj;
+        } else {
+          run += tj;
+        }
+      }
+    }
+  } else {
+    for (int j0 = 0; j0 < C && jstar < 0; j0 += kSampleBatch) {
+#pragma unroll
+      for (int q = 0; q < kSampleBatch; ++q) fetch(j0 + q, buf[q]);
+#pragma unroll
+      for (int q = 0; q < kSampleBatch; ++q) {
+        if (jstar < 0) {
+          const uint64_t sj = (uint64_t)unit_sum<IN_T, TAU1, true>(buf[q], m, inv_tau);
+          const uint64_t tj = wave_sum_u64_dpp(sj);
+          if (theta < run + tj) {
+            jstar = j0 + q;
+            sstar = sj;
+            t = buf[q];
+          } else {
+            run += tj;
+          }
+        }
+      }
+    }
+  }
+  jstar = max(jstar, 0);  // found unless the sums disagree; keeps indexes in the row
+  const uint64_t incl = wave_incl_scan_u64(sstar, lane);
+  uint64_t acc = run + incl - sstar;
+  int tok = -1;
+  if (acc <= theta && theta < acc + sstar) {
+    if constexpr (CH > 0 && CH <= 8) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        if (j == jstar) t = buf[j];
+    } else if constexpr (CH > 0) {
+      fetch(jstar, t);  // one unit of the row, read again by this lane only
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc += (uint64_t)exp_fixed(unit_x<IN_T, TAU1, true>(t, k, inv_tau) - m);
+      if (tok < 0 && acc > theta) tok = (ubase + 64 * jstar) * 8 + k;
     }
   }
   const uint64_t found = __ballot(tok >= 0);
   const int first = found ? (int)__builtin_ctzll(found) : 0;
-  const int t = __builtin_amdgcn_readlane(tok, first);
-  if (lane == 0) tgt[rowi] = max(t, 0);
+  const int y = __builtin_amdgcn_readlane(tok, first);
+  if (lane == 0) tgt[rowi] = max(y, 0);
 }
 
 template <typename IN_T>
@@ -414,13 +654,44 @@ AcceptWork accept_carve(void* ws, int batch, int T) {
   return w;
 }
 
+template <typename IN_T, bool TAU1>
+void launch_sample_rows(const AcceptArgs& a, float inv_tau, uint64_t seed, uint64_t offset,
+                        int32_t* tgt, hipStream_t st) {
+  const int nunit = (a.V + 7) / 8;
+  const int per = (nunit + kSampleBlock - 1) / kSampleBlock;
+  const bool al = (a.V % 8 == 0) && (reinterpret_cast<uintptr_t>(a.target_logits) % 16 == 0);
+  const dim3 grid(a.batch * a.T), block(kSampleBlock);
+#define DDT_SAMPLE(CHV, ALV)                                                                    \
+  hipLaunchKernelGGL((k_sample<IN_T, CHV, ALV, TAU1>), grid, block, 0, st, a, inv_tau, seed, \
+                     offset, per, tgt)
+  if (!al) DDT_SAMPLE(0, false);
+  else if (per <= 1) DDT_SAMPLE(1, true);
+  else if (per <= 2) DDT_SAMPLE(2, true);
+  else if (per <= 4) DDT_SAMPLE(4, true);
+  else if (per <= 8) DDT_SAMPLE(8, true);
+  else {
+    // past 12 units per lane a row in registers leaves one workgroup per CU
+    // (loads, sums and search in series); streamed rows run two per CU
+    if constexpr (sizeof(IN_T) == 2) {
+      if (per <= 12) DDT_SAMPLE(12, true);
+      else DDT_SAMPLE(0, true);
+    } else {
+      DDT_SAMPLE(0, true);
+    }
+  }
+#undef DDT_SAMPLE
+}
+
 hipError_t launch_accept_sample(const AcceptArgs& a, float inv_tau, uint64_t seed,
                                 uint64_t offset, int32_t* tgt, hipStream_t st) {
-  dim3 grid(a.batch * a.T);
-  if (a.dtype == 0)
-    hipLaunchKernelGGL(k_sample<uint16_t>, grid, dim3(256), 0, st, a, inv_tau, seed, offset, tgt);
-  else
-    hipLaunchKernelGGL(k_sample<float>, grid, dim3(256), 0, st, a, inv_tau, seed, offset, tgt);
+  const bool one = inv_tau == 1.0f;
+  if (a.dtype == 0) {
+    if (one) launch_sample_rows<uint16_t, true>(a, inv_tau, seed, offset, tgt, st);
+    else launch_sample_rows<uint16_t, false>(a, inv_tau, seed, offset, tgt, st);
+  } else {
+    if (one) launch_sample_rows<float, true>(a, inv_tau, seed, offset, tgt, st);
+    else launch_sample_rows<float, false>(a, inv_tau, seed, offset, tgt, st);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   AcceptArgs w = a;

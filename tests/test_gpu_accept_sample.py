@@ -155,3 +155,28 @@ def test_accept_sample_full_size_workloads(name):
     o = oracle.accept_sample(tl, tree["tokens"], tree["parents"], tree["num_nodes"], w.L, 1.0,
                              w.seed, 11)
     _same(g, o)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_accept_sample_overflowing_products(dtype):
+    """Logits whose product with 1/temperature overflows to +inf (ranked as
+    -inf, like NaN and +inf logits), next to rows that stay finite; and a
+    temperature whose reciprocal is +inf (every value ranked -inf except the
+    negative ones' -inf products: token 0)."""
+    B, L, V, K, N = 2, 4, 3000, 4, 20
+    tree = _tree(B, L, V, K, N, seed=12)
+    tl = torch.randn(B, N + 1, V) * 2.0
+    tl[0, 0, 10] = 3e37                             # product 3e38 at tau 0.1: finite
+    tl[0, 1, 11] = 3.3e37                           # product overflows: -inf
+    tl[0, 1, 12] = 1e30
+    tl[0, 2, ::5] = 3.39e38                         # many overflowing values
+    tl[0, 3, 7] = float("inf")
+    tl[0, 3, 8] = float("nan")
+    tl[1, 0, :] = 3.39e38                           # every product overflows: token 0
+    tl = tl.to(dtype)
+    for tau in (0.1, 1.0, 1e-39):
+        note("accept_sample overflow %s tau=%g" % (dtype, tau))
+        g = _gpu_sample(tl, tree, L, tau, 5, 2)
+        o = oracle.accept_sample(tl, tree["tokens"], tree["parents"], tree["num_nodes"], L, tau,
+                                 5, 2)
+        _same(g, o)
