@@ -51,13 +51,15 @@ def lib():
         L.oracle_tree.restype = ctypes.c_int
         for name in ("oracle_mask", "oracle_build", "oracle_attn_rows",
                      "oracle_argmax_rows", "oracle_walk", "oracle_accept",
-                     "oracle_philox4x32_10", "oracle_accept_sample"):
+                     "oracle_philox4x32_10", "oracle_accept_sample", "oracle_commit_kv"):
             getattr(L, name).restype = None
         L.oracle_sample_row.restype = ctypes.c_int
         L.oracle_sample_row.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                         ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int]
         L.oracle_accept_sample.argtypes = [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 3 + \
             [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64] + [ctypes.c_void_p] * 5
+        L.oracle_commit_kv.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t] + \
+            [ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_int64] + [ctypes.c_void_p] * 2
         _lib = L
     return _lib
 
@@ -262,3 +264,30 @@ def accept_sample(target_logits, tokens, parents, num_nodes, L: int, tau: float,
                                _p(out["accepted_nodes"]), _p(out["accept_len"]), _p(out["bonus"]),
                                _p(out["target_tokens"]))
     return out
+
+
+def commit_kv(k_cache, v_cache, kv_offsets, prefix_lens, accept_len, accepted_nodes, bonus,
+              T: int):
+    """KV compaction of the accepted path and the bonus hand-off, on copies of
+    the caches ([rows, Hkv, D], float32 or bfloat16). Returns the compacted
+    caches (raw arrays of the same dtype code as the inputs), the new prefix
+    lengths and the next roots."""
+    kr, dt = as_raw(k_cache)
+    vr, dt2 = as_raw(v_cache)
+    assert dt == dt2 and kr.shape == vr.shape
+    kr, vr = kr.copy(), vr.copy()
+    rows = kr.shape[0]
+    row_bytes = kr[0].nbytes if rows else 0
+    offs = np.ascontiguousarray(np.asarray(
+        kv_offsets.detach().cpu().numpy() if hasattr(kv_offsets, "detach") else kv_offsets,
+        dtype=np.int64))
+    P = _i32(prefix_lens)
+    n = _i32(accept_len)
+    a = _i32(accepted_nodes)
+    bo = _i32(bonus)
+    B, L = a.shape
+    newp = np.zeros(B, np.int32)
+    roots = np.zeros(B, np.int32)
+    lib().oracle_commit_kv(_p(kr), _p(vr), row_bytes, _p(offs), _p(P), _p(n), _p(a), _p(bo), B,
+                           L, int(T), rows, _p(newp), _p(roots))
+    return dict(k=kr, v=vr, dtype=dt, new_prefix_lens=newp, next_roots=roots)

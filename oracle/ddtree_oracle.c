@@ -21,6 +21,10 @@
  *      naive fp64                                      [BDDT Abstract, App. B]
  *   5. the target's greedy decoding rule (argmax) and the tree walk that
  *      accepts the matched path and emits the bonus token  [BDDT §4.1]
+ *   6. at target temperature > 0, the target's sample per node (Philox
+ *      counter-based uniforms) and the same walk           [BDDT §4.1]
+ *   7. the KV compaction of the accepted path and the bonus hand-off
+ *                                                          [BDDT §4.1]
  *
  * The pages fix no arithmetic for step 1. Because the tree order compares
  * sums of log-probabilities taken at different depths, both implementations
@@ -627,4 +631,55 @@ void oracle_accept_sample(const void *target_logits, int dtype, const int32_t *t
                     accepted_nodes + (size_t)b * L, accept_len + b, bonus + b);
     }
     free(tgt);
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV compaction after the walk, and the bonus hand-off            [BDDT §4.1] */
+/*                                                                          */
+/* Request b's K/V region starts at row kv_offsets[b]; after the verify its */
+/* prefix holds rows [0, P) and the tree rows follow in node order (node i  */
+/* at row P + i). The sequence the round commits is the prefix, the root    */
+/* (node 0, already at row P) and the accepted nodes a_0 .. a_{n-1}: their  */
+/* rows move to P + 1 .. P + n. Every move reads the rows as they were      */
+/* before the first move (a source may be another move's destination). The  */
+/* new prefix length is P + 1 + n and the bonus becomes the next root.      */
+/* A request whose inputs do not describe such a move (n outside            */
+/* [0, min(L, T - 1)], a node index outside [1, T), a negative offset or    */
+/* prefix, or a tree region past total_rows) is left as it is and gets -1   */
+/* for both outputs. Rows are handled whole (row_bytes = Hkv * D * esize).  */
+/* ------------------------------------------------------------------------ */
+void oracle_commit_kv(void *k_cache, void *v_cache, size_t row_bytes, const int64_t *kv_offsets,
+                      const int32_t *prefix_lens, const int32_t *accept_len,
+                      const int32_t *accepted_nodes, const int32_t *bonus, int batch, int L, int T,
+                      int64_t total_rows, int32_t *new_prefix_lens, int32_t *next_roots)
+{
+    char *tmp = (char *)malloc(row_bytes * (size_t)(L > 0 ? L : 1) * 2);
+    for (int b = 0; b < batch; ++b) {
+        const int n = accept_len[b];
+        const int64_t off = kv_offsets[b];
+        const int64_t P = prefix_lens[b];
+        const int32_t *a = accepted_nodes + (size_t)b * L;
+        int ok = n >= 0 && n <= L && n <= T - 1 && off >= 0 && P >= 0 && off + P + T <= total_rows;
+        for (int k = 0; ok && k < n; ++k)
+            if (a[k] < 1 || a[k] >= T)
+                ok = 0;
+        if (!ok) {
+            new_prefix_lens[b] = -1;
+            if (next_roots)
+                next_roots[b] = -1;
+            continue;
+        }
+        void *caches[2] = {k_cache, v_cache};
+        for (int c = 0; c < 2; ++c) {
+            char *base = (char *)caches[c] + (size_t)(off + P) * row_bytes;
+            for (int k = 0; k < n; ++k) /* read every source first */
+                memcpy(tmp + (size_t)k * row_bytes, base + (size_t)a[k] * row_bytes, row_bytes);
+            for (int k = 0; k < n; ++k)
+                memcpy(base + (size_t)(1 + k) * row_bytes, tmp + (size_t)k * row_bytes, row_bytes);
+        }
+        new_prefix_lens[b] = (int32_t)(P + 1 + n);
+        if (next_roots)
+            next_roots[b] = bonus[b];
+    }
+    free(tmp);
 }
