@@ -60,6 +60,9 @@ def lib():
         L.ddtree_accept_sample.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, f32,
                                            ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp, vp, vp,
                                            vp, sz, vp]
+        L.ddtree_commit_kv.restype = i32
+        L.ddtree_commit_kv.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                       i64, vp, vp, vp]
         L.ddtree_accept.restype = i32
         L.ddtree_accept.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp,
                                     vp, vp, sz, vp]
@@ -196,6 +199,20 @@ def ddtree_accept_sample(target_logits: torch.Tensor, tokens: torch.Tensor,
         _ptr(bonus), _ptr(target_tokens), _ptr(workspace), nbytes,
         _stream(stream, tokens.device))
     _check("ddtree_accept_sample", code)
+
+
+def ddtree_commit_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, kv_offsets: torch.Tensor,
+                     prefix_lens: torch.Tensor, accept_len: torch.Tensor,
+                     accepted_nodes: torch.Tensor, bonus: torch.Tensor, T: int,
+                     new_prefix_lens: torch.Tensor, next_roots: Optional[torch.Tensor],
+                     stream=None) -> None:
+    rows, Hkv, D = k_cache.shape
+    batch, L = accepted_nodes.shape
+    code = lib().ddtree_commit_kv(
+        _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(kv_offsets), _ptr(prefix_lens),
+        _ptr(accept_len), _ptr(accepted_nodes), _ptr(bonus), batch, Hkv, D, L, int(T), rows,
+        _ptr(new_prefix_lens), _ptr(next_roots), _stream(stream, k_cache.device))
+    _check("ddtree_commit_kv", code)
 
 
 # ----------------------------------------------------------------- convenience

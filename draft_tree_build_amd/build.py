@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libddtree.so")
-SOURCES = ["abi.hip", "k_build.hip", "k_tree.hip", "k_attn.hip", "k_accept.hip"]
+SOURCES = ["abi.hip", "k_build.hip", "k_tree.hip", "k_attn.hip", "k_accept.hip", "k_commit.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -45,7 +45,7 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         list(ex.map(lambda so: _compile(*so), zip(SOURCES, objs)))
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs

@@ -214,4 +214,40 @@ int ddtree_accept_sample(const void* target_logits, ddtree_dtype dt, const int32
                                          static_cast<hipStream_t>(stream)));
 }
 
+int ddtree_commit_kv(void* k_cache, void* v_cache, ddtree_dtype dt, const int64_t* kv_offsets,
+                     const int32_t* prefix_lens, const int32_t* accept_len,
+                     const int32_t* accepted_nodes, const int32_t* bonus, int batch, int Hkv,
+                     int D, int L, int T, int64_t total_rows, int32_t* new_prefix_lens,
+                     int32_t* next_roots, void* stream) {
+  if (!k_cache || !v_cache || !kv_offsets || !prefix_lens || !accept_len || !accepted_nodes ||
+      !bonus || !new_prefix_lens)
+    return DDTREE_ERR_ARG;
+  if (batch < 1 || Hkv < 1 || D < 1 || L < 1 || T < 1 || total_rows < 1) return DDTREE_ERR_ARG;
+  if (new_prefix_lens == prefix_lens) return DDTREE_ERR_ARG;
+  if (!dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
+  if (L > DDTREE_MAX_L || T > DDTREE_MAX_N + 1 || Hkv > 65535) return DDTREE_ERR_UNSUPPORTED;
+  const long long slice = (long long)D * (dt == DDTREE_BF16 ? 2 : 4);
+  if (slice % 16 != 0 || slice > 1024) return DDTREE_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(k_cache) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(v_cache) % 16 != 0)
+    return DDTREE_ERR_UNSUPPORTED;
+  CommitArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_offsets = kv_offsets;
+  a.prefix_lens = prefix_lens;
+  a.accept_len = accept_len;
+  a.accepted_nodes = accepted_nodes;
+  a.bonus = bonus;
+  a.batch = batch;
+  a.Hkv = Hkv;
+  a.L = L;
+  a.T = T;
+  a.cpr = (int)(slice / 16);
+  a.total_rows = total_rows;
+  a.new_prefix_lens = new_prefix_lens;
+  a.next_roots = next_roots;
+  return hip_status(launch_commit(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

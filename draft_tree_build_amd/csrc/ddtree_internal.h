@@ -119,6 +119,23 @@ hipError_t launch_accept(const AcceptArgs& a, const AcceptWork& w, hipStream_t s
 hipError_t launch_accept_sample(const AcceptArgs& a, float inv_tau, uint64_t seed, uint64_t offset,
                                 int32_t* tgt, hipStream_t stream);
 
+// ---------------------------------------------------------------- commit
+struct CommitArgs {
+  void* k_cache;
+  void* v_cache;
+  const int64_t* kv_offsets;
+  const int32_t* prefix_lens;
+  const int32_t* accept_len;
+  const int32_t* accepted_nodes;  // [batch, L]
+  const int32_t* bonus;
+  int batch, Hkv, L, T;
+  int cpr;                        // 16-byte chunks per head slice of a row (D * esize / 16)
+  int64_t total_rows;
+  int32_t* new_prefix_lens;
+  int32_t* next_roots;            // may be null
+};
+hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace ddt

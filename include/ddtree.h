@@ -215,6 +215,37 @@ int ddtree_accept_sample(const void *target_logits, ddtree_dtype dt, const int32
                          int32_t *bonus, int32_t *target_tokens, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/*
+ * ddtree_commit_kv -- KV compaction of the accepted path, bonus hand-off.
+ *                                                                [BDDT §4.1]
+ * After the verify, request b's tree K/V rows follow its prefix in node
+ * order (node i at row kv_offsets[b] + prefix_lens[b] + i, as
+ * ddtree_verify_attn reads them). The round commits the root (node 0, in
+ * place) and the accepted nodes a_k = accepted_nodes[b, k], k < n =
+ * accept_len[b]: row P + a_k moves to row P + 1 + k in both caches, every
+ * move reading the rows as they were before the first (a source may be
+ * another move's destination). Rows that receive no move keep their values.
+ * new_prefix_lens[b] = P + 1 + n and next_roots[b] = bonus[b] (the next
+ * round's root). A request whose inputs describe no such move (n outside
+ * [0, min(L, T - 1)], a node index outside [1, T), a negative offset or
+ * prefix, or kv_offsets[b] + P + T > total_rows) is left untouched and gets
+ * -1 in both outputs; this is checked on the device and is not an error.
+ *
+ *   k_cache, v_cache  [total_rows, Hkv, D] dt, 16-byte aligned   in/out (in place)
+ *   kv_offsets        [batch] int64, prefix_lens [batch] int32   in (as for the verify)
+ *   accept_len, accepted_nodes [batch, L], bonus [batch] int32   in (ddtree_accept output)
+ *   T                 tree rows per request (N + 1)
+ *   new_prefix_lens   [batch] int32                              out; must not be prefix_lens
+ *   next_roots        [batch] int32 or NULL                      out
+ * Limits: 1 <= L <= 64, T <= 1025, D * esize a multiple of 16 and at most
+ * 1024 bytes, Hkv <= 65535.
+ */
+int ddtree_commit_kv(void *k_cache, void *v_cache, ddtree_dtype dt, const int64_t *kv_offsets,
+                     const int32_t *prefix_lens, const int32_t *accept_len,
+                     const int32_t *accepted_nodes, const int32_t *bonus, int batch, int Hkv,
+                     int D, int L, int T, int64_t total_rows, int32_t *new_prefix_lens,
+                     int32_t *next_roots, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = ctypes.CDLL(api.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -141,6 +141,28 @@ def _sample(**kw):
 def test_accept_sample_rejects(kw, code):
     _no_gpu()
     assert _sample(**kw) == code
+
+
+def _commit(**kw):
+    a = dict(k=P, v=P, dt=0, offs=P, pl=P, alen=P, accn=P, bonus=P, batch=2, Hkv=8, D=128, L=16,
+             T=65, rows=10000, newp=ctypes.c_void_p(0x2000), roots=N0)
+    a.update(kw)
+    return api.lib().ddtree_commit_kv(a["k"], a["v"], a["dt"], a["offs"], a["pl"], a["alen"],
+                                      a["accn"], a["bonus"], a["batch"], a["Hkv"], a["D"], a["L"],
+                                      a["T"], a["rows"], a["newp"], a["roots"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=N0), ERR_ARG), (dict(accn=N0), ERR_ARG), (dict(newp=N0), ERR_ARG),
+    (dict(newp=P), ERR_ARG),                      # new prefix lengths over the old ones
+    (dict(batch=0), ERR_ARG), (dict(L=0), ERR_ARG), (dict(T=0), ERR_ARG), (dict(rows=0), ERR_ARG),
+    (dict(dt=4), ERR_UNSUP), (dict(L=65), ERR_UNSUP), (dict(T=1026), ERR_UNSUP),
+    (dict(D=100), ERR_UNSUP), (dict(D=1024), ERR_UNSUP), (dict(dt=1, D=257), ERR_UNSUP),
+    (dict(k=ctypes.c_void_p(0x1008)), ERR_UNSUP), (dict(Hkv=70000), ERR_UNSUP),
+])
+def test_commit_rejects(kw, code):
+    _no_gpu()
+    assert _commit(**kw) == code
 
 
 def test_mask_rejects():
