@@ -7,7 +7,10 @@ A step is one whole round on one batch of synthetic input: ddtree_build
 attention over the prefix KV) and ddtree_accept (target argmax + walk; with
 --target-temp T > 0, ddtree_accept_sample: a sample of the target's softmax at
 temperature T per node, then the walk), all enqueued on the current HIP
-stream. Inputs are resident in HBM before the
+stream. --commit-kv adds a fourth stage, ddtree_commit_kv (the accepted
+path's K/V rows moved behind the prefix, in place); so that the walk
+accepts a path, the target logits then carry, at every node, its first
+child's token as their maximum. Inputs are resident in HBM before the
 timed region; several copies rotate from step to step so that a step's
 reads come from HBM rather than from the 256 MB last-level cache.
 
@@ -40,11 +43,13 @@ KERNEL_SOURCES = {
     "verify": ["draft_tree_build_amd/csrc/k_attn.hip"],
     "accept": ["draft_tree_build_amd/csrc/k_accept.hip"],
     "accept_sample": ["draft_tree_build_amd/csrc/k_accept.hip"],
+    "commit": ["draft_tree_build_amd/csrc/k_commit.hip"],
 }
 KERNEL_NAMES = {"build": "ddtree_build: k_rows (+ k_rows_sum for split rows), k_tree",
                 "verify": "ddtree_verify_attn: k_attn_mfma (+ k_attn_combine for split keys)",
                 "accept": "ddtree_accept: k_argmax, k_walk",
-                "accept_sample": "ddtree_accept_sample: k_sample, k_walk"}
+                "accept_sample": "ddtree_accept_sample: k_sample, k_walk",
+                "commit": "ddtree_commit_kv: k_commit"}
 SAMPLE_SEED = 0x5EED
 
 
@@ -52,8 +57,9 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(w, prefix_lens, num_nodes, depths, esize):
-    """Bytes (and flops) each stage must move per step, by its definition."""
+def algorithmic_work(w, prefix_lens, num_nodes, depths, esize, moved_rows=0):
+    """Bytes (and flops) each stage must move per step, by its definition;
+    moved_rows: accepted K/V rows not already in place (commit stage)."""
     B, L, V, K, T = w.batch, w.L, w.V, w.K, w.T
     W = (T + 63) // 64
     build_bytes = B * L * V * esize + B * L * K * 8 + B * T * (4 * 4 + W * 8)
@@ -65,8 +71,9 @@ def algorithmic_work(w, prefix_lens, num_nodes, depths, esize):
     verify_flops = 4.0 * w.Hq * w.D * sum(T * p for p in P)
     verify_flops += 4.0 * w.Hq * w.D * anc
     accept_bytes = sum(int(n) for n in num_nodes) * V * esize
+    commit_bytes = moved_rows * w.Hkv * w.D * esize * 2 * 2 + B * (8 + 4 * (4 + L) + 8)
     return dict(build_bytes=build_bytes, verify_bytes=verify_bytes, verify_flops=verify_flops,
-                accept_bytes=accept_bytes)
+                accept_bytes=accept_bytes, commit_bytes=commit_bytes)
 
 
 def source_hash(rels):
@@ -140,6 +147,9 @@ def main():
     ap.add_argument("--target-temp", type=float, default=0.0,
                     help="target temperature of the acceptance (0: greedy arg-max; > 0: "
                          "ddtree_accept_sample)")
+    ap.add_argument("--commit-kv", action="store_true",
+                    help="add the KV compaction of the accepted path as a fourth stage (target "
+                         "logits then lead the walk down first children)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -164,6 +174,22 @@ def main():
     q_cpu, k_cpu, v_cpu = synth.qkv(w, P_cpu)
     tl_cpu = synth.target_logits(w)
     esize = 2 if w.dtype == "bf16" else 4
+    if args.commit_kv:
+        # the drafted tree does not depend on the target: build it once, then
+        # give every node's first child's token the largest target logit
+        probe = api.Round(w.batch, w.L, w.V, w.K, w.N, dev)
+        probe.build(x_cpu.to(dev), roots_cpu.to(dev), tau)
+        torch.cuda.synchronize()
+        toks, pars = probe.tokens.cpu(), probe.parents.cpu()
+        nn_cpu = probe.num_nodes.cpu()
+        del probe
+        for b in range(w.batch):
+            planted = set()
+            for c in range(1, int(nn_cpu[b])):
+                p = int(pars[b, c])
+                if p not in planted:                    # first child only: one maximum per row
+                    planted.add(p)
+                    tl_cpu[b, p, int(toks[b, c])] = 100.0   # logits are ~N(0, sigma <= 3)
     step_bytes = sum(t.numel() * t.element_size() for t in (x_cpu, q_cpu, k_cpu, v_cpu, tl_cpu))
     R = 1
     if args.rotate_mb > 0:
@@ -180,12 +206,15 @@ def main():
     rnd = api.Round(w.batch, w.L, w.V, w.K, w.N, dev, w.Hq, w.Hkv, w.D, int(w.prefix[1]),
                     dtype=w.torch_dtype)
 
+    if args.commit_kv:
+        rnd.prepare_commit()
     stages = (
         lambda c: rnd.build(c[0], roots, tau),
         lambda c: rnd.verify(c[1], c[2], c[3], offs, P),
         (lambda c: rnd.accept_sample(c[4], args.target_temp, SAMPLE_SEED, 0))
         if args.target_temp > 0 else (lambda c: rnd.accept(c[4])),
-    )
+    ) + ((lambda c: rnd.commit(c[2], c[3], offs, P),) if args.commit_kv else ())
+    stage_names = ("build", "verify", "accept", "commit")[:len(stages)]
     accept_kind = "accept_sample" if args.target_temp > 0 else "accept"
 
     log("warmup %d steps (eager)" % args.warmup)
@@ -224,7 +253,8 @@ def main():
 
     sampled = [i for i in range(args.steps)
                if graphs_off(args) or i % SAMPLE_EVERY == SAMPLE_EVERY - 1] or [args.steps - 1]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for i in sampled}
     log("timing %d steps (%d with stage events)" % (args.steps, len(sampled)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -235,14 +265,14 @@ def main():
             whole[c].replay()
             continue
         ev[0].record()
-        for k in range(3):
+        for k in range(len(stages)):
             stages[k](copies[c])
             ev[k + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     stage_us = {}
-    for k, name in enumerate(("build", "verify", "accept")):
+    for k, name in enumerate(stage_names):
         stage_us[name] = sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in sampled) * 1e3 / len(sampled)
     value = nodes_per_step / (ms_per_step * 1e-3)
     log("ms/step %.4f  stages(us) %s" % (ms_per_step, {k: round(v, 2) for k, v in stage_us.items()}))
@@ -254,7 +284,13 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
-    work = algorithmic_work(w, P_cpu.tolist(), num_nodes.tolist(), rnd.depths.cpu().tolist(), esize)
+    moved = 0
+    if args.commit_kv:
+        alen, anodes = rnd.accept_len.cpu().tolist(), rnd.accepted_nodes.cpu().tolist()
+        moved = sum(1 for b in range(w.batch) for k in range(alen[b]) if anodes[b][k] != k + 1)
+        log("accepted %s, %d rows moved per step" % (alen[:8], moved))
+    work = algorithmic_work(w, P_cpu.tolist(), num_nodes.tolist(), rnd.depths.cpu().tolist(), esize,
+                            moved)
     dom = max(stage_us, key=stage_us.get)
     t_s = stage_us[dom] * 1e-6
     if dom == "verify":
@@ -287,7 +323,9 @@ def main():
                 "Q/K/V ~N(0,1))",
         "config": {"workload": w.name, "batch": w.batch, "L": w.L, "V": w.V, "K": w.K, "N": w.N,
                    "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                   "draft_temp": tau, "target_temp": args.target_temp, "input_copies": R, "hip_graphs": bool(args.graphs),
+                   "draft_temp": tau, "target_temp": args.target_temp,
+                   "commit_kv": bool(args.commit_kv), "input_copies": R,
+                   "hip_graphs": bool(args.graphs),
                    "stage_event_steps": len(sampled)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": roofline,

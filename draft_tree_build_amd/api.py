@@ -268,6 +268,20 @@ class Round:
                       self.accepted, self.accepted_nodes, self.accept_len, self.bonus,
                       self.target_argmax, self.ws_accept, stream)
 
+    def commit(self, k_cache, v_cache, kv_offsets, prefix_lens, stream=None):
+        """KV compaction of the last accepted paths; new prefix lengths and
+        next roots go to ``new_prefix_lens`` and ``next_roots``."""
+        if not hasattr(self, "new_prefix_lens"):
+            raise RuntimeError("Round.commit needs buffers: call Round.prepare_commit() first")
+        ddtree_commit_kv(k_cache, v_cache, kv_offsets, prefix_lens, self.accept_len,
+                         self.accepted_nodes, self.bonus, self.T, self.new_prefix_lens,
+                         self.next_roots, stream)
+
+    def prepare_commit(self):
+        dev = self.tokens.device
+        self.new_prefix_lens = torch.empty(self.batch, dtype=torch.int32, device=dev)
+        self.next_roots = torch.empty(self.batch, dtype=torch.int32, device=dev)
+
     def accept_sample(self, target_logits, temperature: float, seed: int, offset: int,
                       stream=None):
         """Acceptance at target temperature > 0; the sampled token per node

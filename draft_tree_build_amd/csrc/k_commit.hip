@@ -28,26 +28,31 @@ constexpr int kCommitPer = 16;  // chunks per thread: 64 rows x 64 chunks / 256 
 
 __global__ __launch_bounds__(kCommitBlock) void k_commit(CommitArgs a) {
   __shared__ int s_ok, s_n;
+  __shared__ int64_t s_row0;
   __shared__ int32_t s_src[64];
   const int b = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
   const int tid = threadIdx.x;
   if (tid < 64) {  // wave 0 validates the request
+    // every input of the request is requested in one round trip
+    int32_t bonus = a.bonus[b];
     const int n = a.accept_len[b];
     const int64_t off = a.kv_offsets[b];
     const int64_t P = a.prefix_lens[b];
+    const int32_t listed = tid < a.L ? a.accepted_nodes[(size_t)b * a.L + tid] : 0;
+    asm volatile("" : "+v"(bonus));  // keeps the load beside the others
     bool ok = n >= 0 && n <= a.L && n <= a.T - 1 && off >= 0 && P >= 0 &&
               off + P + a.T <= a.total_rows;
-    int src = 0;
-    if (ok && tid < n) src = a.accepted_nodes[(size_t)b * a.L + tid];
+    const int src = (ok && tid < n) ? listed : 0;
     const bool bad = ok && tid < n && (src < 1 || src >= a.T);
     ok = ok && __ballot(bad) == 0;
     s_src[tid] = src;
     if (tid == 0) {
       s_ok = ok;
       s_n = n;
+      s_row0 = off + P;
       if (h == 0 && which == 0) {
         a.new_prefix_lens[b] = ok ? (int32_t)(P + 1 + n) : -1;
-        if (a.next_roots) a.next_roots[b] = ok ? a.bonus[b] : -1;
+        if (a.next_roots) a.next_roots[b] = ok ? bonus : -1;
       }
     }
   }
@@ -56,20 +61,25 @@ __global__ __launch_bounds__(kCommitBlock) void k_commit(CommitArgs a) {
   if (!s_ok || n == 0) return;
   const int cpr = a.cpr;
   const int total = n * cpr;
-  const int64_t row0 = a.kv_offsets[b] + a.prefix_lens[b];
+  const int64_t row0 = s_row0;
   uint4* base = static_cast<uint4*>(which ? a.v_cache : a.k_cache);
   // chunk c of head h in row r of the region: ((row0 + r) * Hkv + h) * cpr + c
-  uint4 val[kCommitPer];
-  int dst[kCommitPer];
+  int kq[kCommitPer], srcq[kCommitPer];
 #pragma unroll
   for (int q = 0; q < kCommitPer; ++q) {
     const int id = tid + q * kCommitBlock;
-    const bool in = id < total;
-    const int k = in ? id / cpr : 0;
-    const int c = in ? id - k * cpr : 0;
-    const int src = s_src[k];
-    dst[q] = (in && src != k + 1) ? k : -1;
-    val[q] = base[((row0 + src) * a.Hkv + h) * cpr + c];
+    kq[q] = id < total ? id / cpr : -1;
+    srcq[q] = s_src[kq[q] < 0 ? 0 : kq[q]];
+  }
+  // all source indices are in registers before the first load is formed
+#pragma unroll
+  for (int q = 0; q < kCommitPer; ++q) asm volatile("" : "+v"(srcq[q]));
+  uint4 val[kCommitPer];
+#pragma unroll
+  for (int q = 0; q < kCommitPer; ++q) {
+    const int id = tid + q * kCommitBlock;
+    const int c = kq[q] < 0 ? 0 : id - kq[q] * cpr;
+    val[q] = base[((row0 + srcq[q]) * a.Hkv + h) * cpr + c];
   }
   // every value has arrived before any thread passes the barrier
 #pragma unroll
@@ -78,10 +88,10 @@ __global__ __launch_bounds__(kCommitBlock) void k_commit(CommitArgs a) {
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < kCommitPer; ++q) {
-    if (dst[q] >= 0) {
+    const int k = kq[q];
+    if (k >= 0 && srcq[q] != k + 1) {  // rows already in place are not rewritten
       const int id = tid + q * kCommitBlock;
-      const int c = id - dst[q] * cpr;
-      base[((row0 + 1 + dst[q]) * a.Hkv + h) * cpr + c] = val[q];
+      base[((row0 + 1 + k) * a.Hkv + h) * cpr + (id - k * cpr)] = val[q];
     }
   }
 }
