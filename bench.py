@@ -20,12 +20,14 @@ divided by the time per step.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
 import os
 import sys
 import time
+import types
 
 import torch
 
@@ -132,39 +134,9 @@ def cpu_baseline(w, inputs, nodes_per_step, budget_s, target_temp):
                                                   el))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(synth.WORKLOADS))
-    ap.add_argument("--rotate-mb", type=int, default=768,
-                    help="rotate input copies until their total exceeds this (0: one copy)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graphs", dest="graphs", action="store_false",
-                    help="launch the ABI calls eagerly instead of replaying captured HIP graphs")
-    ap.add_argument("--target-temp", type=float, default=0.0,
-                    help="target temperature of the acceptance (0: greedy arg-max; > 0: "
-                         "ddtree_accept_sample)")
-    ap.add_argument("--commit-kv", action="store_true",
-                    help="add the KV compaction of the accepted path as a fourth stage (target "
-                         "logits then lead the walk down first children)")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 256 MiB device copy (counter calibration)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a HIP device", file=sys.stderr)
-        sys.exit(2)
-    api.lib()  # fail loudly if the library is not built
-
-    w = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
+def measure(w, args, dev):
+    """Time whole rounds of workload w (the timed region of the contract);
+    returns the measurement and what the report needs."""
     tau = w.taus[0]
     log("workload %s: generating inputs" % w.name)
     x_cpu, _ = synth.drafter_logits(w)
@@ -276,6 +248,80 @@ def main():
         stage_us[name] = sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in sampled) * 1e3 / len(sampled)
     value = nodes_per_step / (ms_per_step * 1e-3)
     log("ms/step %.4f  stages(us) %s" % (ms_per_step, {k: round(v, 2) for k, v in stage_us.items()}))
+    return types.SimpleNamespace(
+        w=w, tau=tau, x_cpu=x_cpu, roots_cpu=roots_cpu, P_cpu=P_cpu, offs_cpu=offs_cpu,
+        q_cpu=q_cpu, k_cpu=k_cpu, v_cpu=v_cpu, tl_cpu=tl_cpu, esize=esize, R=R, rnd=rnd,
+        stage_us=stage_us, value=value, ms_per_step=ms_per_step, nodes_per_step=nodes_per_step,
+        num_nodes=num_nodes, sampled=sampled, accept_kind=accept_kind)
+
+
+def budget_sweep(w, args, dev, budgets):
+    """Whole rounds of workload w at each node budget N (the cost side of the
+    budget trade-off): one JSON line with a record per budget."""
+    recs = []
+    for N in budgets:
+        wn = dataclasses.replace(w, N=N, name="%s@N%d" % (w.name, N))
+        m = measure(wn, args, dev)
+        recs.append({"N": N, "ms_per_step": round(m.ms_per_step, 5),
+                     "nodes_per_step": m.nodes_per_step, "value": round(m.value, 1),
+                     "stages_us": {k: round(v, 3) for k, v in m.stage_us.items()}})
+        del m
+        torch.cuda.empty_cache()
+    out = {"metric": "round time vs node budget (build+tree-attn+accept), 1 GPU", "unit": "ms",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+           "dtype": w.dtype, "data": "synthetic (seeded)",
+           "config": {"workload": w.name, "batch": w.batch, "L": w.L, "V": w.V, "K": w.K,
+                      "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                      "target_temp": args.target_temp, "hip_graphs": bool(args.graphs)},
+           "sweep": recs}
+    print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(synth.WORKLOADS))
+    ap.add_argument("--rotate-mb", type=int, default=768,
+                    help="rotate input copies until their total exceeds this (0: one copy)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graphs", dest="graphs", action="store_false",
+                    help="launch the ABI calls eagerly instead of replaying captured HIP graphs")
+    ap.add_argument("--target-temp", type=float, default=0.0,
+                    help="target temperature of the acceptance (0: greedy arg-max; > 0: "
+                         "ddtree_accept_sample)")
+    ap.add_argument("--commit-kv", action="store_true",
+                    help="add the KV compaction of the accepted path as a fourth stage (target "
+                         "logits then lead the walk down first children)")
+    ap.add_argument("--budgets", default="",
+                    help="comma-separated node budgets N: time whole rounds at each (one JSON "
+                         "line with a record per budget) instead of the single measurement")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(2)
+    api.lib()  # fail loudly if the library is not built
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    if args.budgets:
+        budget_sweep(w, args, dev, [int(x) for x in args.budgets.split(",")])
+        return
+    m = measure(w, args, dev)
+    (tau, x_cpu, roots_cpu, P_cpu, offs_cpu, q_cpu, k_cpu, v_cpu, tl_cpu, esize, R, rnd, stage_us,
+     value, ms_per_step, nodes_per_step, num_nodes, sampled, accept_kind) = (
+        m.tau, m.x_cpu, m.roots_cpu, m.P_cpu, m.offs_cpu, m.q_cpu, m.k_cpu, m.v_cpu, m.tl_cpu,
+        m.esize, m.R, m.rnd, m.stage_us, m.value, m.ms_per_step, m.nodes_per_step, m.num_nodes,
+        m.sampled, m.accept_kind)
 
     if args.copy_probe:
         a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
