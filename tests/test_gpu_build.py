@@ -34,10 +34,11 @@ CASES = [
     (1, 6, 1001, 5, 25, torch.float32),       # unaligned f32
     (3, 8, 5000, 8, 64, torch.bfloat16),      # 512 threads, 4 vectors per thread
     (1, 16, 32000, 8, 64, torch.bfloat16),    # 8 vectors per thread
-    (2, 7, 60000, 16, 100, torch.bfloat16),   # 16 vectors per thread
+    (2, 7, 60000, 16, 100, torch.bfloat16),   # split rows, 29 chunks
     (1, 5, 60000, 16, 100, torch.float32),
-    (2, 4, 151936, 16, 50, torch.bfloat16),   # 40 vectors per thread
-    (1, 3, 151936, 8, 20, torch.float32),     # streaming
+    (2, 4, 151936, 16, 50, torch.bfloat16),   # split rows, 32 chunks
+    (16, 16, 151936, 8, 40, torch.bfloat16),  # 256 rows: split, 10 chunks of <= 2048 vectors
+    (1, 3, 151936, 8, 20, torch.float32),     # split rows, f32
     (1, 3, 400000, 32, 40, torch.bfloat16),   # streaming
 ]
 
