@@ -101,6 +101,76 @@ def load_traffic(workload, stage):
     return ent.get("bytes_per_launch")
 
 
+def measured_peaks(dev):
+    """Peaks measured on this device, outside the timed region, for the
+    roofline fractions beside the published ones: HBM = bytes per second of
+    one streaming read of 4 GiB (ddtree_probe_hbm_read; a 1 GiB device copy,
+    read plus written bytes, is reported beside it); MFMA = bf16 flops per
+    second of a dense v_mfma_f32_32x32x16_bf16 loop (ddtree_probe_mfma_bf16,
+    two workgroups per compute unit)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    grid = 8 * cus
+    fold = torch.empty(grid, dtype=torch.int32, device=dev)
+    hbm_read = n / timed(lambda: api.ddtree_probe_hbm_read(src, fold, grid), 10) / 1e9
+    a, b = src[: 1 << 30], src[1 << 30: 2 << 30]
+    hbm_copy = 2.0 * (1 << 30) / timed(lambda: b.copy_(a), 10) / 1e9
+    del src, fold, a, b
+    grid, iters = 2 * cus, 4096
+    out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    mfma = grid * 4 * 4 * iters * 32768.0 / timed(
+        lambda: api.ddtree_probe_mfma_bf16(out, grid, iters), 5) / 1e12
+    del out
+    torch.cuda.empty_cache()
+    return {"hbm_GBs": round(hbm_read, 1), "hbm_how": "streaming read of 4 GiB (ddtree_probe_hbm_read)",
+            "hbm_copy_GBs": round(hbm_copy, 1),
+            "bf16_mfma_TFs": round(mfma, 1),
+            "bf16_mfma_how": "v_mfma_f32_32x32x16_bf16 loop, 4 chains per wave, 2 workgroups per CU "
+                             "(ddtree_probe_mfma_bf16)"}
+
+
+def stage_rooflines(work, stage_us, peaks):
+    """Each stage's algorithmic work over its event time, against the
+    published peak and the measured one, on its binding roofline."""
+    out = {}
+    for name, us in stage_us.items():
+        t_s = us * 1e-6
+        if name == "verify":
+            t_mem = work["verify_bytes"] / (HBM_PEAK_GBS * 1e9)
+            t_mma = work["verify_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+        else:
+            t_mem, t_mma = 1.0, 0.0
+        if t_mma > t_mem:
+            ach = work["verify_flops"] / t_s / 1e12
+            rec = dict(bound="mfma", unit="TFLOP/s", peak=MFMA_BF16_PEAK_TFS,
+                       peak_measured=peaks["bf16_mfma_TFs"] if peaks else None)
+        else:
+            ach = work[name + "_bytes"] / t_s / 1e9
+            rec = dict(bound="hbm", unit="GB/s", peak=HBM_PEAK_GBS,
+                       peak_measured=peaks["hbm_GBs"] if peaks else None)
+        rec["achieved"] = round(ach, 3)
+        rec["frac"] = round(ach / rec["peak"], 5)
+        rec["frac_measured"] = round(ach / rec["peak_measured"], 5) if rec["peak_measured"] else None
+        rec["us"] = round(us, 3)
+        out[name] = rec
+    return out
+
+
 def graphs_off(args):
     return not args.graphs
 
@@ -300,6 +370,8 @@ def main():
                          "line with a record per budget) instead of the single measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--no-peak-probe", dest="peak_probe", action="store_false",
+                    help="skip measuring the device's copy bandwidth and bf16 GEMM rate")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -350,10 +422,17 @@ def main():
         nbytes = work[dom + "_bytes"]
         achieved, peak, unit, bound = nbytes / t_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
     kname = accept_kind if dom == "accept" else dom
+    peaks = None
+    if args.peak_probe:
+        log("measuring device peaks (copy bandwidth, bf16 GEMM)")
+        peaks = measured_peaks(dev)
+    stages_rl = stage_rooflines(work, stage_us, peaks)
     roofline = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
                     frac=round(achieved / peak, 5), traffic=load_traffic(w.name, kname),
                     kernel=KERNEL_NAMES[kname], stage=kname,
-                    avg_launch_us=round(stage_us[dom], 3))
+                    avg_launch_us=round(stage_us[dom], 3),
+                    peak_measured=stages_rl[dom]["peak_measured"],
+                    frac_measured=stages_rl[dom]["frac_measured"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -375,6 +454,8 @@ def main():
                    "stage_event_steps": len(sampled)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": roofline,
+        "stages_roofline": stages_rl,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

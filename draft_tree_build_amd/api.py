@@ -66,6 +66,10 @@ def lib():
         L.ddtree_accept.restype = i32
         L.ddtree_accept.argtypes = [vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp,
                                     vp, vp, sz, vp]
+        L.ddtree_probe_mfma_bf16.restype = i32
+        L.ddtree_probe_mfma_bf16.argtypes = [vp, i32, i32, vp]
+        L.ddtree_probe_hbm_read.restype = i32
+        L.ddtree_probe_hbm_read.argtypes = [vp, i64, vp, i32, vp]
         _lib = L
     return _lib
 
@@ -289,3 +293,17 @@ class Round:
         ddtree_accept_sample(target_logits, self.tokens, self.parents, self.num_nodes, self.L,
                              temperature, seed, offset, self.accepted, self.accepted_nodes,
                              self.accept_len, self.bonus, self.target_argmax, None, stream)
+
+
+# ---------------------------------------------------------------- calibration
+def ddtree_probe_mfma_bf16(out: torch.Tensor, grid: int, iters: int, stream=None) -> None:
+    """Dense bf16 MFMA loop (measurement only): grid * 4 * 4 * iters * 32768 flops."""
+    _check("ddtree_probe_mfma_bf16", lib().ddtree_probe_mfma_bf16(
+        _ptr(out), int(grid), int(iters), _stream(stream, out.device)))
+
+
+def ddtree_probe_hbm_read(src: torch.Tensor, out: torch.Tensor, grid: int, stream=None) -> None:
+    """One streaming read of src (measurement only)."""
+    _check("ddtree_probe_hbm_read", lib().ddtree_probe_hbm_read(
+        _ptr(src), src.numel() * src.element_size(), _ptr(out), int(grid),
+        _stream(stream, src.device)))

@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libddtree.so")
-SOURCES = ["abi.hip", "k_build.hip", "k_tree.hip", "k_attn.hip", "k_accept.hip", "k_commit.hip"]
+SOURCES = ["abi.hip", "k_build.hip", "k_tree.hip", "k_attn.hip", "k_accept.hip", "k_commit.hip",
+           "k_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -250,4 +250,16 @@ int ddtree_commit_kv(void* k_cache, void* v_cache, ddtree_dtype dt, const int64_
   return hip_status(launch_commit(a, static_cast<hipStream_t>(stream)));
 }
 
+int ddtree_probe_mfma_bf16(float* out, int grid, int iters, void* stream) {
+  if (!out || grid < 1 || grid > (1 << 20) || iters < 1 || iters > (1 << 20)) return DDTREE_ERR_ARG;
+  return hip_status(launch_probe_mfma(out, grid, iters, static_cast<hipStream_t>(stream)));
+}
+
+int ddtree_probe_hbm_read(const void* src, int64_t bytes, uint32_t* out, int grid, void* stream) {
+  if (!src || !out || bytes < 16 || bytes % 16 != 0 || grid < 1 || grid > (1 << 20))
+    return DDTREE_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return DDTREE_ERR_ARG;
+  return hip_status(launch_probe_read(src, bytes, out, grid, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

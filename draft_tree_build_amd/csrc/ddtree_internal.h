@@ -136,6 +136,11 @@ struct CommitArgs {
 };
 hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- calibration
+hipError_t launch_probe_mfma(float* out, int grid, int iters, hipStream_t stream);
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* out, int grid,
+                             hipStream_t stream);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace ddt

@@ -246,6 +246,28 @@ int ddtree_commit_kv(void *k_cache, void *v_cache, ddtree_dtype dt, const int64_
                      int D, int L, int T, int64_t total_rows, int32_t *new_prefix_lens,
                      int32_t *next_roots, void *stream);
 
+/*
+ * Calibration (measurement only; no part of a DDTree round calls these).
+ * They give the measured peaks that roofline fractions are also reported
+ * against, beside the published ones. Asynchronous on `stream`; the caller
+ * times them (e.g. with events on that stream).
+ *
+ * ddtree_probe_mfma_bf16 -- grid workgroups of 256 threads; every wave runs
+ * four independent chains of `iters` v_mfma_f32_32x32x16_bf16 operations
+ * (32768 flops each), so one call performs grid * 4 * 4 * iters * 32768
+ * flops with no memory traffic but the final stores.
+ *   out   [grid * 256] float, device      out (sums of the accumulators)
+ * Returns DDTREE_ERR_ARG for a null out or grid / iters outside [1, 2^20].
+ *
+ * ddtree_probe_hbm_read -- reads `bytes` from src once in 16-byte vectors
+ * (grid workgroups of 256 threads, eight loads in flight per thread).
+ *   src   device, 16-byte aligned, bytes a positive multiple of 16       in
+ *   out   [grid] uint32, device           out (one folded word per workgroup)
+ * Returns DDTREE_ERR_ARG for null pointers, misalignment or a bad size.
+ */
+int ddtree_probe_mfma_bf16(float *out, int grid, int iters, void *stream);
+int ddtree_probe_hbm_read(const void *src, int64_t bytes, uint32_t *out, int grid, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,12 +19,12 @@ OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP = 0, -1, -2, -3, -4
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ddtree_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ddtree_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     L = ctypes.CDLL(api.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -171,3 +171,21 @@ def test_mask_rejects():
     assert L.ddtree_mask(None, P, 1, 9, P, None) == ERR_ARG
     assert L.ddtree_mask(P, P, 0, 9, P, None) == ERR_ARG
     assert L.ddtree_mask(P, P, 1, 2000, P, None) == ERR_UNSUP
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.ddtree_probe_mfma_bf16(None, 1, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_mfma_bf16(P, 0, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_mfma_bf16(P, 1, 0, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_mfma_bf16(P, (1 << 20) + 1, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_hbm_read(None, 16, P, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_hbm_read(P, 16, None, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_hbm_read(P, 24, P, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_hbm_read(P, 0, P, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_hbm_read(ctypes.c_void_p(0x1008), 16, P, 1, None), ERR_ARG),
+    (lambda L: L.ddtree_probe_hbm_read(P, 16, P, 0, None), ERR_ARG),
+])
+def test_probes_reject(call, code):
+    """The calibration kernels' host checks (measurement only)."""
+    _no_gpu()
+    assert call(api.lib()) == code
