@@ -16,7 +16,9 @@
 // fragments come out transposed through ds_read_b64_tr_b16. Per wave and
 // tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
 // (lane = query row), online softmax in fp32 (exp2 domain), O^T += V^T P^T
-// with P split into two bf16 parts (hi + lo) so the weights stay ~fp32 exact.
+// on v_mfma_f32_32x32x16_f16: each V tile is converted to fp16 in LDS once
+// (every wave converts the rows it staged), and P enters as fp16 (2^-12
+// relative per weight, against 2^-9 for bf16 weights).
 // The key tile list is prefix tiles then tree tiles (mask applied); long
 // lists are split across workgroups and merged by a second kernel
 // (log-sum-exp weights).
@@ -44,11 +46,34 @@ constexpr float kLog2e = 1.4426950408889634f;
 // chunk each) and the V transpose reads (4 consecutive keys, 2 chunks each)
 // free of bank conflicts.
 constexpr int kTileBytes = kKeys * kD * 2;  // 16 KB
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short short8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
+
+// bf16 -> fp16 in place for the four 1 KB blocks of a V tile that wave w
+// staged (bytes 4096 w .. 4096 w + 4095; 16 bytes per lane and block). The
+// conversion is exact for |v| in [2^-14, 65504]; smaller values round to
+// fp16 subnormals (absolute error <= 2^-25). Called after the wave's own
+// DMA has landed and before the barrier that publishes the tile.
+__device__ __forceinline__ void v_tile_to_f16(unsigned char* vbuf, int w, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint4* p = reinterpret_cast<uint4*>(vbuf + (4 * w + j) * 1024 + 16 * lane);
+    const uint4 u = *p;
+    const uint32_t in[4] = {u.x, u.y, u.z, u.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx2 f = {__uint_as_float(in[q] << 16), __uint_as_float(in[q] & 0xFFFF0000u)};
+      o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, halfx2));
+    }
+    *p = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
 
 struct AttnSplit {
   int nsplit;
@@ -243,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       }
     }
     // V fragments of the first half, read while the scores are computed
-    auto read_v = [&](int kb, bf16x8 (&vf)[4][2]) __attribute__((always_inline)) {
+    auto read_v = [&](int kb, halfx8 (&vf)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -251,10 +276,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
           const int kofs = (32 * kb + 16 * hf) * 256;
           const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][0] + kofs));
           const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][1] + kofs));
-          vf[db][hf] = __builtin_bit_cast(bf16x8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+          vf[db][hf] = __builtin_bit_cast(halfx8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
         }
     };
-    bf16x8 vf[4][2];
+    halfx8 vf[4][2];
     read_v(0, vf);
 
     // ---- mask (tree tiles and the ragged last prefix tile only) and row max.
@@ -293,48 +318,38 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    // P is carried as a pair of bf16 MFMA operands, P = hi + lo with
-    // hi = bf16(p) and lo = bf16(p - hi): |p - hi - lo| <= 2^-18 p, so the
-    // weights keep ~fp32 accuracy even when only a few keys contribute.
+    // P enters the MFMA as fp16: weights are below 2^8, so fp16 keeps
+    // 2^-12 of each (subnormal below 2^-14, absolute error <= 2^-25).
     float psum = 0.0f;
-    auto probs = [&](int kb, bf16x8 (&pf)[2], bf16x8 (&pl)[2]) __attribute__((always_inline)) {
+    auto probs = [&](int kb, halfx8 (&pf)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        bf16x2 hi2[4], lo2[4];
+        halfx2 h2[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           floatx2 pr;
           pr[0] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2], c_log2, -m_use));
           pr[1] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2 + 1], c_log2, -m_use));
           psum += pr[0] + pr[1];
-          hi2[e2] = __builtin_convertvector(pr, bf16x2);
-          const uint32_t hb = __builtin_bit_cast(uint32_t, hi2[e2]);
-          floatx2 rest = {pr[0] - __uint_as_float(hb << 16), pr[1] - __uint_as_float(hb & 0xFFFF0000u)};
-          lo2[e2] = __builtin_convertvector(rest, bf16x2);
+          h2[e2] = __builtin_convertvector(pr, halfx2);
         }
-        pf[hf] = bf16x8{hi2[0][0], hi2[0][1], hi2[1][0], hi2[1][1],
-                        hi2[2][0], hi2[2][1], hi2[3][0], hi2[3][1]};
-        pl[hf] = bf16x8{lo2[0][0], lo2[0][1], lo2[1][0], lo2[1][1],
-                        lo2[2][0], lo2[2][1], lo2[3][0], lo2[3][1]};
+        pf[hf] = halfx8{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
       }
     };
-    auto pv = [&](const bf16x8 (&vfr)[4][2], const bf16x8 (&pf)[2], const bf16x8 (&pl)[2])
-        __attribute__((always_inline)) {
+    auto pv = [&](const halfx8 (&vfr)[4][2], const halfx8 (&pf)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[db][hf], pl[hf], acc_o[db], 0, 0, 0);
-        }
+        for (int hf = 0; hf < 2; ++hf)
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
     };
-    bf16x8 pf0[2], pl0[2];
-    probs(0, pf0, pl0);
-    pv(vf, pf0, pl0);
-    bf16x8 pf1[2], pl1[2];
-    probs(1, pf1, pl1);
+    halfx8 pf0[2];
+    probs(0, pf0);
+    pv(vf, pf0);
+    halfx8 pf1[2];
+    probs(1, pf1);
     read_v(1, vf);
-    pv(vf, pf1, pl1);
+    pv(vf, pf1);
     l_run = l_run * alpha + psum;
   };
 
@@ -347,6 +362,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     mword_next = load_mword(t_begin);
   }
   __builtin_amdgcn_s_waitcnt(0);
+  if (t_begin < t_end) v_tile_to_f16(v_lds0, w, lane);
   __syncthreads();
   for (int t = t_begin; t < t_end; t += 2) {
     {
@@ -357,6 +373,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       }
       tile_body(t, mword, k_lds0, v_lds0);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
+      if (t + 1 < t_end) v_tile_to_f16(v_lds1, w, lane);
       __syncthreads();
     }
     if (t + 1 < t_end) {
@@ -367,6 +384,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       }
       tile_body(t + 1, mword, k_lds1, v_lds1);
       __builtin_amdgcn_s_waitcnt(0);
+      if (t + 2 < t_end) v_tile_to_f16(v_lds0, w, lane);
       __syncthreads();
     }
   }

@@ -136,8 +136,13 @@ int ddtree_mask(const int32_t *parents, const int32_t *num_nodes, int batch, int
  *   softmax_scale <= 0 selects 1/sqrt(D)
  *   workspace     >= ddtree_verify_workspace_size(...) bytes
  *
- * bf16: fp32 accumulation on MFMA, bf16 output. f32: fp32 throughout.
- * Limits: Hq % Hkv == 0; T <= 1025; D in {32, 64, 128} (bf16: D = 128).
+ * bf16: q.k on bf16 MFMA with fp32 accumulation; softmax in fp32; the
+ * P.V product on fp16 MFMA (weights rounded to fp16, 2^-12 relative; V
+ * converted to fp16, exact for |v| in [2^-14, 65504], values below that
+ * range rounded to fp16 subnormals, values above it overflow); fp32
+ * accumulation, bf16 output. f32: fp32 throughout.
+ * Limits: Hq % Hkv == 0; T <= 1025; D in {32, 64, 128} (bf16: D = 128);
+ * bf16 V within +-65504.
  */
 size_t ddtree_verify_workspace_size(ddtree_dtype dt, int batch, int T, int Hq, int Hkv, int D,
                                     int max_prefix_len);
