@@ -411,7 +411,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     return;
   }
 
-  // ---- split: write this split's partial (unnormalised O, m, l)
+  // ---- split: write this split's partial (unnormalised O, m, l), streamed
+  // past the L2 (nontemporal): read once by the merge kernel, they would
+  // otherwise wait dirty in L2 for the end-of-kernel write-back (measured:
+  // 16.5 -> 14.9 us at a 2048-key prefix, merge 4.0 -> 4.3 us)
   const int Rpad = row_tiles * kTileRows;
   const size_t bh = (size_t)bhi;
   const size_t nbh = (size_t)a.batch * a.Hkv;
@@ -423,12 +426,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       for (int j = 0; j < 4; ++j) {
         floatx4 v4 = {acc_o[db][4 * j], acc_o[db][4 * j + 1], acc_o[db][4 * j + 2],
                       acc_o[db][4 * j + 3]};
-        *reinterpret_cast<floatx4*>(po + 32 * db + 8 * j + 4 * gq) = v4;
+        __builtin_nontemporal_store(v4, reinterpret_cast<floatx4*>(po + 32 * db + 8 * j + 4 * gq));
       }
     if (gq == 0) {
       float* pm = part_ml + (((size_t)z * nbh + bh) * Rpad + row) * 2;
-      pm[0] = m_run;
-      pm[1] = l_row;
+      __builtin_nontemporal_store(m_run, pm);
+      __builtin_nontemporal_store(l_row, pm + 1);
     }
   }
 }
