@@ -147,8 +147,11 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
   int n = 1;
 
   // One pop; OVER: keep candidates behind the lanes in the overflow list.
-  auto pop = [&](auto over_tag) __attribute__((always_inline)) {
-    constexpr bool OVER = decltype(over_tag)::value;
+  // MODE 0: lanes only; 1: lanes and the overflow list; 2: lanes only,
+  // counting the occupied lanes in h (the window cannot overflow yet)
+  auto pop = [&](auto mode_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool OVER = MODE == 1;
     const uint32_t xh = rdlane(Hh, 0), xl = rdlane(Hl, 0), xps = rdlane(Hps, 0);
     rec_h = wrlane(rec_h, xh, (uint32_t)(n & 63));
     rec_l = wrlane(rec_l, xl, (uint32_t)(n & 63));
@@ -196,6 +199,8 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
       h += (in1 ? 1 : 0) + (in2 ? 1 : 0) - 1;
     }
 
+    if constexpr (MODE == 2) h += (c1 != kEmpty ? 1 : 0) + (c2 != kEmpty ? 1 : 0) - 1;
+
     // rebuild the lanes
     const uint32_t slh = dpp_shift<kShl1>(kNone, Hh), sll = dpp_shift<kShl1>(kNone, Hl);
     const uint32_t srh = dpp_zero<kShr1>(Hh), srl = dpp_zero<kShr1>(Hl);
@@ -213,6 +218,13 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
   };
 
   if (N > 64) {
+    // While at most 62 lanes are occupied a pop cannot push a candidate
+    // behind the lanes (it removes one and adds at most two): the overflow
+    // bookkeeping starts only when the window is about to fill.
+    for (; n <= N && h <= 62; ++n) {
+      if (rdlane(Hh, 0) == kNone) break;
+      pop(std::integral_constant<int, 2>{});
+    }
     for (; n <= N; ++n) {
       if (h == 0) {
         if (nover == 0) break;  // the tree holds every node the tables allow
@@ -235,7 +247,7 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
         omin = nover > 0 ? sh.over[0] : kEmpty;
         h = take;
       }
-      pop(std::true_type{});
+      pop(std::integral_constant<int, 1>{});
       if (h >= N - n) {  // the lanes cover every remaining pop
         ++n;
         break;
@@ -245,7 +257,7 @@ __device__ int tree_pops(TreeShared& sh, int L, int K, int N) {
   // every remaining pop is served by the lanes; a dry lane array ends the tree
   for (; n <= N; ++n) {
     if (rdlane(Hh, 0) == kNone) break;
-    pop(std::false_type{});
+    pop(std::integral_constant<int, 0>{});
   }
   sh.nkey[((n - 1) & ~63) + lane] = key64(rec_h, rec_l);
   return n;
