@@ -38,6 +38,8 @@ CASES = [
     (1, 5, 60000, 16, 100, torch.float32),
     (2, 4, 151936, 16, 50, torch.bfloat16),   # split rows, 32 chunks
     (16, 16, 151936, 8, 40, torch.bfloat16),  # 256 rows: split, 10 chunks of <= 2048 vectors
+    (16, 16, 32768, 8, 70, torch.bfloat16),   # 256 rows of 4096 vectors: whole rows, 8 per thread
+    (16, 16, 32776, 8, 70, torch.bfloat16),   # 256 rows of 4097 vectors: split, 3 chunks
     (1, 3, 151936, 8, 20, torch.float32),     # split rows, f32
     (1, 3, 400000, 32, 40, torch.bfloat16),   # streaming
 ]
