@@ -78,18 +78,25 @@ __device__ __forceinline__ void v_tile_to_f16(unsigned char* vbuf, int w, int la
 struct AttnSplit {
   int nsplit;
   int row_tiles;
-  int total;    // work items: batch * Hkv * nsplit * row_tiles
-  int per_xcd;  // work items per XCD slice of the grid
+  int chunk;        // splits per unit
+  int unit_chunks;  // units per (request, kv-head): ceil(nsplit / chunk)
+  int units;        // batch * Hkv * unit_chunks
+  int per_xcd;      // workgroups per XCD: ceil(units / 8) * chunk * row_tiles
 };
 
 constexpr int kXcds = 8;
 
 // One workgroup = 128 query rows of one (request, kv-head) over one range of
 // key tiles. Grid: 1-D, XCD-aware -- consecutive workgroup ids go to
-// different XCDs, so work item w runs as workgroup (w % per_xcd) * 8 + w /
-// per_xcd, which keeps all row tiles of one (request, kv-head, split) on one
-// XCD and its K/V tiles in that XCD's L2. Key tiles are double-buffered in
-// LDS: tile t+1 is fetched into registers while tile t is computed.
+// different XCDs, so XCD x runs workgroups x, x + 8, ... Units of work --
+// one (request, kv-head) with a run of `chunk` consecutive splits, all their
+// row tiles -- are dealt to the XCDs in turn, unit u to XCD u % 8: the row
+// tiles of a split share its K/V tiles in one L2, the splits of a unit share
+// its Q rows, and every request is spread over the XCDs, which keeps them
+// evenly loaded when prefix lengths differ. Splits are cut into several
+// units only when there are fewer (request, kv-head) pairs than XCDs. Key
+// tiles are double-buffered in LDS: tile t+1 is fetched into registers while
+// tile t is computed.
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, float* part_o,
                                                       float* part_ml) {
   // two buffers of K and V tiles; 64 KB
@@ -98,13 +105,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   __shared__ __attribute__((aligned(16))) unsigned char k_lds1[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds1[kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wi = (int)(blockIdx.x % kXcds) * pl.per_xcd + (int)(blockIdx.x / kXcds);
-  if (wi >= pl.total) return;
   const int nsplit = pl.nsplit, row_tiles = pl.row_tiles;
-  const int xt = wi % row_tiles;
-  const int z = (wi / row_tiles) % nsplit;
-  const int bhi = wi / (row_tiles * nsplit);
-  const int b = bhi / a.Hkv, hk = bhi - (bhi / a.Hkv) * a.Hkv;
+  const int xj = (int)(blockIdx.x / kXcds);  // this workgroup's place on its XCD
+  const int per_unit = pl.chunk * row_tiles;
+  const int u = (xj / per_unit) * kXcds + (int)(blockIdx.x % kXcds);  // unit
+  const int in_unit = xj % per_unit;
+  const int z = (u % pl.unit_chunks) * pl.chunk + in_unit / row_tiles;
+  if (u >= pl.units || z >= nsplit) return;
+  const int xt = in_unit % row_tiles;
+  const int bhi = u / pl.unit_chunks;
+  const int hk = bhi % a.Hkv;
+  // Requests are taken longest prefix first (ties: lower index first), so
+  // that on every XCD the longest workgroups start first and the short ones
+  // fill the tail. Every workgroup ranks the prefix lengths the same way:
+  // lane i holds request i's length and counts the requests ahead of it.
+  int b = bhi / a.Hkv;
+  if (a.batch > 1 && a.batch <= 64) {
+    const int pl_i = lane < a.batch ? max(a.prefix_lens[lane], 0) : -1;
+    int ahead = 0;
+    for (int j = 0; j < a.batch; ++j) {
+      const int pl_j = __builtin_amdgcn_readlane(pl_i, j);
+      ahead += (pl_j > pl_i || (pl_j == pl_i && j < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(lane < a.batch && ahead == b);
+    b = __ffsll((unsigned long long)hit) - 1;
+  }
   const int g = a.Hq / a.Hkv;
   const int T = a.T;
   const int R = T * g;
@@ -416,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   // otherwise wait dirty in L2 for the end-of-kernel write-back (measured:
   // 16.5 -> 14.9 us at a 2048-key prefix, merge 4.0 -> 4.3 us)
   const int Rpad = row_tiles * kTileRows;
-  const size_t bh = (size_t)bhi;
+  const size_t bh = (size_t)b * a.Hkv + hk;  // the merge reads (request, kv-head)
   const size_t nbh = (size_t)a.batch * a.Hkv;
   if (row_valid) {  // rows past num_nodes are zeroed by the merge, which never reads them
     float* po = part_o + (((size_t)z * nbh + bh) * Rpad + row) * kD;
@@ -596,7 +621,7 @@ int device_cus() {
 // CU) times the key tiles per workgroup, plus the partial-result traffic of
 // the merge -- with at least 4 key tiles per split.
 AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int max_prefix_len) {
-  AttnSplit s{1, 0, 0, 0};
+  AttnSplit s{1, 0, 1, 1, 0, 0};
   if (dtype != 0 || D != kD) return s;
   const int g = Hq / Hkv;
   const int R = T * g;
@@ -620,8 +645,11 @@ AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int ma
     }
   }
   s.nsplit = best;
-  s.total = (int)(blocks * best);
-  s.per_xcd = (s.total + kXcds - 1) / kXcds;
+  const long nbh = (long)batch * Hkv;
+  s.chunk = nbh >= kXcds ? best : (int)std::max(1L, best * nbh / kXcds);
+  s.unit_chunks = (best + s.chunk - 1) / s.chunk;
+  s.units = (int)(nbh * s.unit_chunks);
+  s.per_xcd = (s.units + kXcds - 1) / kXcds * s.chunk * s.row_tiles;
   return s;
 }
 

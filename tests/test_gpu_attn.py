@@ -5,7 +5,8 @@ Abstract / §4.1 (one verify pass, ancestor-only mask), App. B. Tolerance:
 |gpu - ref| <= 1e-3 + 2e-2 |ref| for bf16 and 1e-5 + 1e-5 |ref| for f32.
 Small shapes compare every output row (ragged prefixes straddling key tiles,
 trees with padding rows, GQA group sizes 1/4/8, row tiles with a ragged
-tail, the split-KV path); the full-size workloads compare sampled rows in
+tail, the split-KV path with requests of different lengths and with fewer
+(request, kv-head) pairs than XCDs); the full-size workloads compare sampled rows in
 the launch configuration the benchmark times.
 """
 import numpy as np
@@ -55,6 +56,10 @@ SMALL = [
     (1, 16, 80, 8, 64, 32, 8, [2048]),          # split-KV path
     (1, 5, 60, 6, 200, 64, 8, [900]),           # g = 8, many row tiles
     (2, 6, 60, 6, 300, 32, 8, [3000, 1500]),    # split, many row tiles, ragged last row tile
+    (3, 6, 60, 6, 100, 32, 8, [700, 3000, 1500]),  # split, requests taken longest first
+    (2, 6, 60, 6, 100, 32, 8, [1500, 1500]),    # split, equal lengths (ties by index)
+    (1, 16, 80, 8, 64, 32, 4, [4000]),          # 4 (request, kv-head) pairs: splits cut into units
+    (2, 4, 40, 4, 40, 16, 2, [2500, 5000]),     # 4 pairs, ragged, longer request second
 ]
 
 
@@ -93,7 +98,7 @@ def test_attn_f32_all_rows(D):
 
 
 def test_attn_repeatable_split_counters():
-    """The split-KV merge counters are reused: two calls give identical bits."""
+    """Two split-KV calls on one workspace give identical bits (partials rewritten)."""
     B, L, V, K, N, Hq, Hkv, P = 1, 16, 80, 8, 64, 32, 8, [3000]
     T, D = N + 1, 128
     tree = _tree(B, L, V, K, N, seed=1)
