@@ -12,10 +12,16 @@ path's K/V rows moved behind the prefix, in place); so that the walk
 accepts a path, the target logits then carry, at every node, its first
 child's token as their maximum. Inputs are resident in HBM before the
 timed region; several copies rotate from step to step so that a step's
-reads come from HBM rather than from the 256 MB last-level cache.
+reads come from HBM rather than from the 256 MB last-level cache (the
+default workload's inputs, 1.8 GB per step, exceed it with one copy).
+
+Every timed step replays each stage's captured HIP graph with HIP events
+between the stages on the stream the kernels run on, so every stage of
+every timed step is event-timed (mean, median, p10, p90 in the JSON line).
 
 Prints one JSON line. value = sum over requests of (num_nodes - 1) per step
-divided by the time per step.
+divided by the time per step. The CPU baseline is the oracle, timed on one
+thread and on all host cores.
 """
 from __future__ import annotations
 
@@ -37,7 +43,7 @@ sys.path.insert(0, ROOT)
 from draft_tree_build_amd import api, synth  # noqa: E402
 
 METRIC = "verified tree nodes/sec (build+tree-attn+accept) and % HBM roofline, 1 GPU"
-DEFAULT_WORKLOAD = "L16_V32000_K8_N64_P2048"
+DEFAULT_WORKLOAD = "B4_L32_V151936_K16_N512_P65536"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 KERNEL_SOURCES = {
@@ -53,6 +59,7 @@ KERNEL_NAMES = {"build": "ddtree_build: k_rows (+ k_rows_sum for split rows), k_
                 "accept_sample": "ddtree_accept_sample: k_sample, k_walk",
                 "commit": "ddtree_commit_kv: k_commit"}
 SAMPLE_SEED = 0x5EED
+LLC_BYTES = 256 * 2**20        # MI355X last-level (Infinity) cache
 
 
 def log(msg):
@@ -171,37 +178,80 @@ def stage_rooflines(work, stage_us, peaks):
     return out
 
 
-def graphs_off(args):
-    return not args.graphs
+def _pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    pos = (len(xs) - 1) * q
+    lo, hi = int(math.floor(pos)), int(math.ceil(pos))
+    return xs[lo] + (xs[hi] - xs[lo]) * (pos - lo)
 
 
-def cpu_baseline(w, inputs, nodes_per_step, budget_s, target_temp):
-    """The oracle, single-threaded, on whole rounds of the same workload."""
+def _summary(xs):
+    return {"mean": round(sum(xs) / len(xs), 3), "median": round(_pct(xs, 0.5), 3),
+            "p10": round(_pct(xs, 0.1), 3), "p90": round(_pct(xs, 0.9), 3), "n": len(xs)}
+
+
+def cpu_baseline(w, inputs, nodes_per_step, target_temp, attn_seconds):
+    """The oracle as it stands (plain C, not tuned), on the same host tensors:
+    the whole build and the whole accept of one round, and the tree
+    attention of a seeded sample of the round's valid query rows, scaled to
+    all of them (a row's cost is its key count: the prefix plus the node's
+    ancestors). Timed twice: on one thread, and on all the host cores this
+    process may use (the oracle spreads independent drafter rows, requests,
+    query rows and target rows over OpenMP threads; its arithmetic does not
+    change). The sample is sized so that the one-thread attention takes
+    about attn_seconds."""
     import numpy as np
     import oracle
     x, roots, q, k, v, P, offs, tl = inputs
     tau = w.taus[0]
-    sel = [(b, i, h) for b in range(w.batch) for i in range(w.T) for h in range(w.Hq)]
-    rounds, t0 = 0, time.perf_counter()
-    while True:
-        tree = oracle.build_tree(x, roots, w.K, w.N, tau)
-        oracle.attn_rows(q, k, v, offs, P, tree["num_nodes"], tree["mask"], w.T, w.Hq, w.Hkv, w.D,
-                         1.0 / math.sqrt(w.D), sel)
-        if target_temp > 0:
-            oracle.accept_sample(tl, tree["tokens"], tree["parents"], tree["num_nodes"], w.L,
-                                 target_temp, SAMPLE_SEED, rounds)
-        else:
-            oracle.accept(tl, None, tree["tokens"], tree["parents"], tree["num_nodes"], w.L)
-        rounds += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return dict(value=nodes_per_step * rounds / el, unit="nodes/s", cores=1, kind="oracle",
-                sample="%d whole round(s) of %s (build, attention of all %d query rows, %s), "
-                       "single thread, %.1f s" % (rounds, w.name, len(sel),
-                                                  "sampled accept at target temperature %g"
-                                                  % target_temp if target_temp > 0 else "accept",
-                                                  el))
+    cores = oracle.host_cores()
+    tree = oracle.build_tree(x, roots, w.K, w.N, tau)
+    valid = [(b, i, h) for b in range(w.batch) for i in range(int(tree["num_nodes"][b]))
+             for h in range(w.Hq)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(valid))
+    scale = 1.0 / math.sqrt(w.D)
+
+    def attn(sel):
+        t0 = time.perf_counter()
+        oracle.attn_rows(q, k, v, offs, P, tree["num_nodes"], tree["mask"], w.T, w.Hq, w.Hkv,
+                         w.D, scale, sel)
+        return time.perf_counter() - t0
+
+    # size the sample: the one-thread cost of a few rows
+    probe = [valid[j] for j in order[:min(8, len(valid))]]
+    per_row = attn(probe) / len(probe)
+    nsamp = int(min(len(valid), max(16, attn_seconds / max(per_row, 1e-9))))
+    sel = [valid[j] for j in order[:nsamp]]
+    res = {}
+    for nt in sorted({1, cores}):
+        with oracle.threads(nt):
+            t0 = time.perf_counter()
+            tr = oracle.build_tree(x, roots, w.K, w.N, tau)
+            t_build = time.perf_counter() - t0
+            t_attn = attn(sel)
+            t0 = time.perf_counter()
+            if target_temp > 0:
+                oracle.accept_sample(tl, tr["tokens"], tr["parents"], tr["num_nodes"], w.L,
+                                     target_temp, SAMPLE_SEED, 0)
+            else:
+                oracle.accept(tl, None, tr["tokens"], tr["parents"], tr["num_nodes"], w.L)
+            t_accept = time.perf_counter() - t0
+        t_round = t_build + t_attn * len(valid) / len(sel) + t_accept
+        res[nt] = dict(value=round(nodes_per_step / t_round, 3), round_s=round(t_round, 4),
+                       build_s=round(t_build, 4), accept_s=round(t_accept, 4),
+                       attn_sample_s=round(t_attn, 4))
+    acc = "sampled accept at target temperature %g" % target_temp if target_temp > 0 else "greedy accept"
+    return dict(
+        value=res[cores]["value"], unit="nodes/s", cores=cores, kind="oracle",
+        value_1thread=res[1]["value"],
+        sample="one round of %s: the whole build and %s, and the tree attention of %d of the "
+               "round's %d valid query rows (seeded sample), its time scaled by %d/%d; timed on "
+               "%d thread(s) (value) and on 1 thread (value_1thread)"
+               % (w.name, acc, len(sel), len(valid), len(valid), len(sel), cores),
+        timings={("%d_threads" % nt): r for nt, r in res.items()})
 
 
 def measure(w, args, dev):
@@ -267,62 +317,64 @@ def measure(w, args, dev):
     num_nodes = rnd.num_nodes.cpu()
     nodes_per_step = int((num_nodes - 1).sum())
 
-    # Per input copy, one HIP graph holding the whole round. Most timed steps
-    # replay it (no host launch overhead between the ABI calls). Every
-    # SAMPLE_EVERY-th step calls the three ABI functions directly instead,
-    # with HIP events between them on the same stream: those events time each
-    # stage inside the timed region (the graph replays queued ahead keep the
-    # GPU from waiting on the host there). --no-graphs launches every step
-    # directly, with events.
-    SAMPLE_EVERY = 20
-    whole = None
+    # Per input copy and stage, one captured HIP graph (the stage's kernels
+    # with no host launch overhead between them). Every timed step replays
+    # the stages' graphs in order on the current stream with an event before
+    # the first and after each: the events time every stage of every timed
+    # step on the stream the kernels run on. --no-graphs launches the ABI
+    # calls directly instead, with the same events.
+    graphs = None
     if args.graphs:
-        log("capturing %d graphs" % R)
+        log("capturing %d x %d graphs" % (R, len(stages)))
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        whole = []
+        graphs = []
         with torch.cuda.stream(side):
             for c in range(R):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    for f in stages:
+                row = []
+                for f in stages:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=side):
                         f(copies[c])
-                whole.append(g)
+                    row.append(g)
+                graphs.append(row)
         torch.cuda.current_stream().wait_stream(side)
-        for i in range(min(R, args.warmup)):
-            whole[i].replay()
+        for i in range(min(R, max(1, args.warmup))):
+            for g in graphs[i]:
+                g.replay()
         torch.cuda.synchronize()
 
-    sampled = [i for i in range(args.steps)
-               if graphs_off(args) or i % SAMPLE_EVERY == SAMPLE_EVERY - 1] or [args.steps - 1]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-           for i in sampled}
-    log("timing %d steps (%d with stage events)" % (args.steps, len(sampled)))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
+    log("timing %d steps (stage events on every step)" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         c = i % R
-        ev = evs.get(i)
-        if ev is None:
-            whole[c].replay()
-            continue
+        ev = evs[i]
         ev[0].record()
         for k in range(len(stages)):
-            stages[k](copies[c])
+            if graphs is not None:
+                graphs[c][k].replay()
+            else:
+                stages[k](copies[c])
             ev[k + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_us = {}
-    for k, name in enumerate(stage_names):
-        stage_us[name] = sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in sampled) * 1e3 / len(sampled)
+    stage_samples = {name: [evs[i][k].elapsed_time(evs[i][k + 1]) * 1e3 for i in range(args.steps)]
+                     for k, name in enumerate(stage_names)}
+    step_samples = [evs[i][0].elapsed_time(evs[i][-1]) * 1e3 for i in range(args.steps)]
+    stage_us = {k: sum(v) / len(v) for k, v in stage_samples.items()}
     value = nodes_per_step / (ms_per_step * 1e-3)
-    log("ms/step %.4f  stages(us) %s" % (ms_per_step, {k: round(v, 2) for k, v in stage_us.items()}))
+    log("ms/step %.4f  stages(us, mean) %s" % (ms_per_step, {k: round(v, 2) for k, v in stage_us.items()}))
     return types.SimpleNamespace(
         w=w, tau=tau, x_cpu=x_cpu, roots_cpu=roots_cpu, P_cpu=P_cpu, offs_cpu=offs_cpu,
         q_cpu=q_cpu, k_cpu=k_cpu, v_cpu=v_cpu, tl_cpu=tl_cpu, esize=esize, R=R, rnd=rnd,
-        stage_us=stage_us, value=value, ms_per_step=ms_per_step, nodes_per_step=nodes_per_step,
-        num_nodes=num_nodes, sampled=sampled, accept_kind=accept_kind)
+        stage_us=stage_us, stage_stats={k: _summary(v) for k, v in stage_samples.items()},
+        step_stats=_summary(step_samples), value=value, ms_per_step=ms_per_step,
+        nodes_per_step=nodes_per_step, num_nodes=num_nodes, accept_kind=accept_kind,
+        step_bytes=step_bytes)
 
 
 def budget_sweep(w, args, dev, budgets):
@@ -347,15 +399,98 @@ def budget_sweep(w, args, dev, budgets):
     print(json.dumps(out), flush=True)
 
 
+def summarize_traffic(fetch_csv, write_csv, workload, commands):
+    """HBM bytes per launch of every stage from two rocprofv3 counter runs of
+    this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled
+    by what the same counter reads for the plain 256 MiB device copy that
+    --copy-probe runs in the same process. Writes profiles/traffic.json
+    (keyed by workload and stage, with a hash of the kernel sources) and
+    profiles/traffic_<workload>.txt."""
+    import collections
+    import csv
+    import statistics
+
+    def load(path, counter):
+        d = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                n = r["Kernel_Name"].replace("ddt::(anonymous namespace)::", "")
+                n = n.split("(")[0].replace("void ", "")
+                d[n].append(float(r["Counter_Value"]))
+        return d
+
+    F, Wr = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy = [n for n in F if "copyBuffer" in n]
+    if not copy:
+        raise SystemExit("no device copy in the FETCH_SIZE run: profile with --copy-probe")
+    cf, cw = max(F[copy[0]]), max(Wr[copy[0]])
+    copy_kib = 256 * 1024
+    ff, wf = copy_kib / cf, copy_kib / cw
+    stages = {"build": ["k_rows", "k_rows_sum", "k_tree", "k_tree_level"],
+              "verify": ["k_attn_mfma", "k_attn_combine", "k_attn_simple"],
+              "accept": ["k_argmax", "k_walk"], "accept_sample": ["k_sample"],
+              "commit": ["k_commit"]}
+    res = {}
+    for stage, prefixes in stages.items():
+        ks, fsum, wsum = {}, 0.0, 0.0
+        for n in F:
+            if n.split("<")[0] in prefixes:
+                fv, wv = statistics.mean(F[n]), statistics.mean(Wr.get(n, [0.0]))
+                ks[n] = {"fetch_kib_raw": round(fv, 1), "write_kib_raw": round(wv, 1)}
+                fsum += fv
+                wsum += wv
+        if not ks:
+            continue
+        res[stage] = {"bytes_per_launch": int(round((fsum * ff + wsum * wf) * 1024)),
+                      "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                      "fetch_kib_raw": round(fsum, 1), "write_kib_raw": round(wsum, 1),
+                      "kernels": ks, "source_sha": source_hash(KERNEL_SOURCES[stage])}
+    if "accept_sample" in res and "accept" in res:       # k_walk serves both
+        res["accept_sample"]["bytes_per_launch"] += int(round(
+            sum(v["fetch_kib_raw"] * ff + v["write_kib_raw"] * wf
+                for n, v in res["accept"]["kernels"].items() if n.startswith("k_walk")) * 1024))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            allres = json.load(f)
+    except (OSError, ValueError):
+        allres = {}
+    allres[workload] = res
+    with open(path, "w") as f:
+        json.dump(allres, f, indent=1, sort_keys=True)
+    with open(os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload), "w") as f:
+        f.write("HBM traffic per launch, workload %s (rocprofv3 counters, KiB per dispatch "
+                "averaged over dispatches)\n\n" % workload)
+        f.write("commands (from /tmp, TMPDIR=/tmp, REPO = repository root):\n%s\n"
+                "summary: python bench.py --workload %s --summarize-traffic FETCH_CSV WRITE_CSV\n\n"
+                % ("".join("  %s\n" % c for c in commands.split(" ;; ") if c), workload))
+        f.write("calibration: the 256 MiB device copy run by --copy-probe reads FETCH_SIZE %.0f KiB "
+                "and WRITE_SIZE %.0f KiB;\nscale factors fetch %.4f, write %.4f (bytes moved / "
+                "counter)\n\n" % (cf, cw, ff, wf))
+        f.write("%-52s %12s %12s %14s\n" % ("kernel", "FETCH_KiB", "WRITE_KiB", "scaled_MB"))
+        for stage in res:
+            for n, v in sorted(res[stage]["kernels"].items()):
+                f.write("%-52s %12.1f %12.1f %14.3f\n" % (
+                    n[:52], v["fetch_kib_raw"], v["write_kib_raw"],
+                    (v["fetch_kib_raw"] * ff + v["write_kib_raw"] * wf) * 1024 / 1e6))
+        f.write("\n")
+        for stage in res:
+            f.write("stage %-13s scaled bytes per launch: %d\n" % (stage, res[stage]["bytes_per_launch"]))
+    print(json.dumps({k: v["bytes_per_launch"] for k, v in res.items()}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=list(synth.WORKLOADS))
     ap.add_argument("--rotate-mb", type=int, default=768,
                     help="rotate input copies until their total exceeds this (0: one copy)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="one-thread seconds of the oracle's attention sample (CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", dest="graphs", action="store_false",
                     help="launch the ABI calls eagerly instead of replaying captured HIP graphs")
@@ -372,7 +507,18 @@ def main():
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--no-peak-probe", dest="peak_probe", action="store_false",
                     help="skip measuring the device's copy bandwidth and bf16 GEMM rate")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE and "
+                         "a WRITE_SIZE rocprofv3 run of this script (with --copy-probe) into "
+                         "profiles/traffic.json and a text summary for --workload")
+    ap.add_argument("--commands", default="",
+                    help="with --summarize-traffic: the commands that made the runs (recorded)")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload,
+                          args.commands)
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -390,10 +536,10 @@ def main():
         return
     m = measure(w, args, dev)
     (tau, x_cpu, roots_cpu, P_cpu, offs_cpu, q_cpu, k_cpu, v_cpu, tl_cpu, esize, R, rnd, stage_us,
-     value, ms_per_step, nodes_per_step, num_nodes, sampled, accept_kind) = (
+     value, ms_per_step, nodes_per_step, num_nodes, accept_kind) = (
         m.tau, m.x_cpu, m.roots_cpu, m.P_cpu, m.offs_cpu, m.q_cpu, m.k_cpu, m.v_cpu, m.tl_cpu,
         m.esize, m.R, m.rnd, m.stage_us, m.value, m.ms_per_step, m.nodes_per_step, m.num_nodes,
-        m.sampled, m.accept_kind)
+        m.accept_kind)
 
     if args.copy_probe:
         a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
@@ -440,9 +586,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle (%.0f s budget)" % args.cpu_seconds)
+        log("timing the CPU oracle (one thread and all cores)")
         inputs = (x_cpu, roots_cpu, q_cpu, k_cpu, v_cpu, P_cpu.numpy(), offs_cpu.numpy(), tl_cpu)
-        cpu = cpu_baseline(w, inputs, nodes_per_step, args.cpu_seconds, args.target_temp)
+        cpu = cpu_baseline(w, inputs, nodes_per_step, args.target_temp, args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
@@ -454,9 +600,12 @@ def main():
                    "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "draft_temp": tau, "target_temp": args.target_temp,
                    "commit_kv": bool(args.commit_kv), "input_copies": R,
-                   "hip_graphs": bool(args.graphs),
-                   "stage_event_steps": len(sampled)},
+                   "hip_graphs": bool(args.graphs), "stage_event_steps": args.steps,
+                   "cache": "cold" if R > 1 or m.step_bytes > LLC_BYTES else "warm",
+                   "step_input_MB": round(m.step_bytes / 1e6, 1)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "stages_us_stats": m.stage_stats,
+        "step_us_stats": m.step_stats,
         "roofline": roofline,
         "stages_roofline": stages_rl,
         "measured_peaks": peaks,

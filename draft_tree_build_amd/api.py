@@ -20,6 +20,8 @@ BF16 = 0
 F32 = 1
 STATUS_NONFINITE = 1
 STATUS_ALL_NEG_INF = 2
+STATUS_OUT_NONFINITE = 4
+STATUS_BAD_KV = 8
 _lib = None
 
 
@@ -53,7 +55,7 @@ def lib():
         L.ddtree_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.ddtree_verify_attn.restype = i32
         L.ddtree_verify_attn.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                         i32, i64, f32, vp, vp, sz, vp]
+                                         i32, i64, f32, vp, vp, vp, sz, vp]
         L.ddtree_accept_workspace_size.restype = sz
         L.ddtree_accept_workspace_size.argtypes = [i32, i32]
         L.ddtree_accept_sample.restype = i32
@@ -157,13 +159,13 @@ def ddtree_verify_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        kv_offsets: torch.Tensor, prefix_lens: torch.Tensor,
                        num_nodes: torch.Tensor, mask: torch.Tensor, max_prefix_len: int,
                        out: torch.Tensor, workspace: torch.Tensor, softmax_scale: float = 0.0,
-                       stream=None) -> None:
+                       stream=None, status_flags: Optional[torch.Tensor] = None) -> None:
     batch, T, Hq, D = q.shape
     Hkv = k.shape[1]
     code = lib().ddtree_verify_attn(
         _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(kv_offsets), _ptr(prefix_lens),
         _ptr(num_nodes), _ptr(mask), batch, T, Hq, Hkv, D, int(max_prefix_len), k.shape[0],
-        float(softmax_scale), _ptr(out), _ptr(workspace),
+        float(softmax_scale), _ptr(out), _ptr(status_flags), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check("ddtree_verify_attn", code)
 
@@ -263,9 +265,10 @@ class Round:
                      self.depths, self.scores, self.num_nodes, self.mask, self.topk_tokens,
                      self.topk_logprobs, self.status, self.ws_build, stream)
 
-    def verify(self, q, k, v, kv_offsets, prefix_lens, stream=None):
+    def verify(self, q, k, v, kv_offsets, prefix_lens, stream=None, status_flags=None):
         ddtree_verify_attn(q, k, v, kv_offsets, prefix_lens, self.num_nodes, self.mask,
-                           self.max_prefix_len, self.out, self.ws_verify, 0.0, stream)
+                           self.max_prefix_len, self.out, self.ws_verify, 0.0, stream,
+                           status_flags)
 
     def accept(self, target_logits, stream=None):
         ddtree_accept(target_logits, None, self.tokens, self.parents, self.num_nodes, self.L,

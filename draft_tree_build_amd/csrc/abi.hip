@@ -103,8 +103,8 @@ int ddtree_verify_attn(const void* q, const void* k, const void* v, ddtree_dtype
                        const int64_t* kv_offsets, const int32_t* prefix_lens,
                        const int32_t* num_nodes, const uint64_t* mask, int batch, int T, int Hq,
                        int Hkv, int D, int max_prefix_len, int64_t total_rows,
-                       float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       float softmax_scale, void* out, int32_t* status_flags, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !kv_offsets || !prefix_lens || !num_nodes || !mask || !out)
     return DDTREE_ERR_ARG;
   if (batch < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_prefix_len < 0 || total_rows < 1)
@@ -136,6 +136,7 @@ int ddtree_verify_attn(const void* q, const void* k, const void* v, ddtree_dtype
   a.total_rows = total_rows;
   a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf((float)D);
   a.out = out;
+  a.status = status_flags;
   return hip_status(launch_attn(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
@@ -191,6 +192,8 @@ int ddtree_accept_sample(const void* target_logits, ddtree_dtype dt, const int32
   if (!(temperature > 0.0f) || isinf(temperature)) return DDTREE_ERR_ARG;
   if (!dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
   if (T > DDTREE_MAX_N + 1 || L > DDTREE_MAX_L) return DDTREE_ERR_UNSUPPORTED;
+  // each weight is below 2^45: V <= 2^19 keeps the 64-bit row sum exact
+  if (V > DDTREE_MAX_V) return DDTREE_ERR_UNSUPPORTED;
   if ((long long)batch * T > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
   if (!target_tokens && (!workspace || workspace_bytes < accept_workspace_bytes(batch, T)))
     return DDTREE_ERR_WORKSPACE;

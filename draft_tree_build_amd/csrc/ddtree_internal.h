@@ -85,6 +85,7 @@ struct AttnArgs {
   int64_t total_rows;
   float scale;
   void* out;
+  int32_t* status;          // [batch] or null: DDTREE_STATUS_OUT_NONFINITE / _BAD_KV
 };
 size_t attn_workspace_bytes(int dtype, int batch, int T, int Hq, int Hkv, int D,
                             int max_prefix_len);

@@ -75,6 +75,19 @@ __device__ __forceinline__ void v_tile_to_f16(unsigned char* vbuf, int w, int la
   }
 }
 
+// Request b's key rows kv0 .. kv0 + P + T must lie inside the caches; the
+// offsets and lengths may come from earlier kernels, so this is checked here.
+__device__ __forceinline__ bool kv_in_range(int64_t kv0, int P, int T, int64_t total_rows) {
+  return kv0 >= 0 && P >= 0 && kv0 <= total_rows - (int64_t)P - T;
+}
+
+__device__ __forceinline__ void set_status(int32_t* status, int b, int bits) {
+  if (status) atomicOr(status + b, bits);
+}
+
+constexpr int kStatusNonfinite = 4;  // DDTREE_STATUS_OUT_NONFINITE
+constexpr int kStatusBadKv = 8;      // DDTREE_STATUS_BAD_KV
+
 struct AttnSplit {
   int nsplit;
   int row_tiles;
@@ -133,9 +146,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   const int g = a.Hq / a.Hkv;
   const int T = a.T;
   const int R = T * g;
-  const int nn = min(max(a.num_nodes[b], 0), T);
+  const int64_t kv0s = a.kv_offsets[b];
+  const int P = a.prefix_lens[b];
+  const bool kv_ok = kv_in_range(kv0s, P, T, a.total_rows);
+  // a request outside the caches reads no key: all its rows are padding
+  const int nn = kv_ok ? min(max(a.num_nodes[b], 0), T) : 0;
   const int nvalid_rows = nn * g;
   const int tile_row0 = xt * kTileRows;
+  if (!kv_ok && z == 0 && xt == 0 && tid == 0) set_status(a.status, b, kStatusBadKv);
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* Kg = static_cast<const uint16_t*>(a.k);
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v);
@@ -159,7 +177,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   }
 
   // ---- key tiles of this row tile: prefix tiles then tree tiles
-  const int P = max(a.prefix_lens[b], 0);
   const int np = (P + kKeys - 1) / kKeys;
   const int last_row = min(tile_row0 + kTileRows, nvalid_rows) - 1;
   const int max_node = last_row / g;  // ancestors have smaller indices
@@ -167,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   const int ntiles = np + nt;
   const int per = (ntiles + nsplit - 1) / nsplit;
   const int t_begin = min(z * per, ntiles), t_end = min(t_begin + per, ntiles);
-  const size_t kv0 = (size_t)a.kv_offsets[b];
+  const size_t kv0 = (size_t)kv0s;
   const int W = (T + 63) >> 6;
   const float c_log2 = a.scale * kLog2e;
 
@@ -216,17 +233,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   auto dma_tile = [&](int t, unsigned char* kbuf, unsigned char* vbuf) __attribute__((always_inline)) {
     int base, nvalid;
     tile_rows(t, &base, &nvalid);
-    const int64_t r0 = (int64_t)kv0 + base;  // first key row of the tile
-    const bool in_range = r0 < a.total_rows;
-    const int lim = in_range ? (int)min((int64_t)nvalid, a.total_rows - r0) : 0;
-    const size_t tb = in_range ? (size_t)r0 * row_bytes : 0;
+    // every key row of the request is inside the caches (kv_in_range) and a
+    // tile holds at least one valid key
+    const size_t tb = (kv0 + (size_t)base) * row_bytes;
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(Kg) + tb;
     const unsigned char* vt = reinterpret_cast<const unsigned char*>(Vg) + tb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // rows past the tile's end re-read the tile's first row: their scores
-      // are masked, so they only ever meet zero weights
-      const uint32_t off = dma_row[j] < lim ? dma_off[j] : dma_off[j] - (uint32_t)dma_row[j] * row_bytes;
+      // rows past the tile's nvalid keys re-read the tile's first row: their
+      // scores are masked (allow covers keys < nvalid only), so they only
+      // ever meet zero weights
+      const uint32_t off = dma_row[j] < nvalid ? dma_off[j] : dma_off[j] - (uint32_t)dma_row[j] * row_bytes;
       unsigned char* kd = kbuf + (4 * w + j) * 1024;
       unsigned char* vd = vbuf + (4 * w + j) * 1024;
       __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
@@ -417,6 +434,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   const float l_row = l_run + __shfl_xor(l_run, 32, 64);
 
   if (nsplit == 1) {
+    bool bad = false;
     if (row < R) {
       const float inv = (row_valid && l_row > 0.0f) ? 1.0f / l_row : 0.0f;
       uint16_t* o = O + (((size_t)b * T + node) * a.Hq + head) * kD;
@@ -426,6 +444,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
         for (int j = 0; j < 4; ++j) {
           floatx2 lo2 = {acc_o[db][4 * j] * inv, acc_o[db][4 * j + 1] * inv};
           floatx2 hi2 = {acc_o[db][4 * j + 2] * inv, acc_o[db][4 * j + 3] * inv};
+          bad |= !__builtin_isfinite(lo2[0]) | !__builtin_isfinite(lo2[1]) |
+                 !__builtin_isfinite(hi2[0]) | !__builtin_isfinite(hi2[1]);
           bf16x2 l2 = __builtin_convertvector(lo2, bf16x2);
           bf16x2 h2 = __builtin_convertvector(hi2, bf16x2);
           bf16x4 o4 = {l2[0], l2[1], h2[0], h2[1]};
@@ -433,6 +453,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
         }
       }
     }
+    // a non-finite output (an infinite fp16 V value, or a non-finite input)
+    // is reported once per wave
+    if (__ballot(bad) != 0ull && lane == 0) set_status(a.status, b, kStatusNonfinite);
     return;
   }
 
@@ -479,7 +502,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int nsplit, in
   const int R = T * g;
   const int rr = blockIdx.x * kRows + rl;
   if (rr >= R) return;
-  const int nn = min(max(a.num_nodes[b], 0), T);
+  const bool kv_ok = kv_in_range(a.kv_offsets[b], a.prefix_lens[b], T, a.total_rows);
+  const int nn = kv_ok ? min(max(a.num_nodes[b], 0), T) : 0;
   const int nd = rr / g, hd = hk * g + (rr - nd * g);
   uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * T + nd) * a.Hq + hd) * kD + 4 * c4;
   if (rr >= nn * g) {
@@ -531,17 +555,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int nsplit, in
   bf16x2 h2 = __builtin_convertvector(hi2, bf16x2);
   bf16x4 o4 = {l2[0], l2[1], h2[0], h2[1]};
   *reinterpret_cast<bf16x4*>(o) = o4;
+  const bool bad = !__builtin_isfinite(lo2[0]) | !__builtin_isfinite(lo2[1]) |
+                   !__builtin_isfinite(hi2[0]) | !__builtin_isfinite(hi2[1]);
+  if (bad) set_status(a.status, b, kStatusNonfinite);
 }
 
 // ------------------------------------------------------------------ fp32 path
-template <typename IN_T>
-__device__ __forceinline__ float load_f(const IN_T* p, size_t i) {
-  if constexpr (sizeof(IN_T) == 2) return bf16_to_float(p[i]);
-  else return p[i];
-}
-
 // One thread per query row (b, i, h); fp32 online softmax over the allowed keys.
-template <typename IN_T, int D>
+template <int D>
 __global__ __launch_bounds__(128) void k_attn_simple(AttnArgs a) {
   const int64_t rid = (int64_t)blockIdx.x * 128 + threadIdx.x;
   const int64_t nrows = (int64_t)a.batch * a.T * a.Hq;
@@ -549,22 +570,24 @@ __global__ __launch_bounds__(128) void k_attn_simple(AttnArgs a) {
   const int h = (int)(rid % a.Hq);
   const int i = (int)((rid / a.Hq) % a.T);
   const int b = (int)(rid / ((int64_t)a.Hq * a.T));
-  const IN_T* Q = static_cast<const IN_T*>(a.q);
-  const IN_T* Kg = static_cast<const IN_T*>(a.k);
-  const IN_T* Vg = static_cast<const IN_T*>(a.v);
-  IN_T* O = static_cast<IN_T*>(a.out);
+  const float* Q = static_cast<const float*>(a.q);
+  const float* Kg = static_cast<const float*>(a.k);
+  const float* Vg = static_cast<const float*>(a.v);
+  float* O = static_cast<float*>(a.out);
   const size_t obase = (((size_t)b * a.T + i) * a.Hq + h) * D;
   float acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.0f;
-  const int nn = min(max(a.num_nodes[b], 0), a.T);
+  const bool kv_ok = kv_in_range(a.kv_offsets[b], a.prefix_lens[b], a.T, a.total_rows);
+  const int nn = kv_ok ? min(max(a.num_nodes[b], 0), a.T) : 0;
+  if (!kv_ok && i == 0 && h == 0) set_status(a.status, b, kStatusBadKv);
   float l = 0.0f;
   if (i < nn) {
     float q[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) q[d] = load_f(Q, obase + d);
+    for (int d = 0; d < D; ++d) q[d] = Q[obase + d];
     const int g = a.Hq / a.Hkv, hk = h / g;
-    const int P = max(a.prefix_lens[b], 0);
+    const int P = a.prefix_lens[b];
     const size_t kv0 = (size_t)a.kv_offsets[b];
     const int W = (a.T + 63) >> 6;
     const uint64_t* mrow = a.mask + ((size_t)b * a.T + i) * W;
@@ -575,31 +598,36 @@ __global__ __launch_bounds__(128) void k_attn_simple(AttnArgs a) {
         const int t = j - P;
         if (((mrow[t >> 6] >> (t & 63)) & 1ull) == 0) continue;
       }
-      if ((int64_t)(kv0 + j) >= a.total_rows) continue;
       const size_t kb = ((kv0 + j) * a.Hkv + hk) * D;
       float s = 0.0f;
 #pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(q[d], load_f(Kg, kb + d), s);
+      for (int d = 0; d < D; ++d) s = fmaf(q[d], Kg[kb + d], s);
       s *= c;
       const float mn = fmaxf(m, s);
       const float alpha = exp2f(m - mn);
       const float p = exp2f(s - mn);
       l = l * alpha + p;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, load_f(Vg, kb + d), acc[d] * alpha);
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vg[kb + d], acc[d] * alpha);
       m = mn;
     }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  bool bad = false;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     const float o = acc[d] * inv;
-    if constexpr (sizeof(IN_T) == 2) {
-      O[obase + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
-    } else {
-      O[obase + d] = o;
-    }
+    bad |= !__builtin_isfinite(o);
+    O[obase + d] = o;
   }
+  if (bad) set_status(a.status, b, kStatusNonfinite);
+}
+
+// Clears the per-request status words before the attention kernels OR bits
+// into them.
+__global__ void k_zero_status(int32_t* status, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) status[i] = 0;
 }
 
 // Compute units of the current device (cached per device id).
@@ -653,14 +681,13 @@ AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int ma
   return s;
 }
 
-template <typename IN_T>
 hipError_t launch_simple(const AttnArgs& a, hipStream_t st) {
   const int64_t nrows = (int64_t)a.batch * a.T * a.Hq;
   dim3 grid((unsigned)((nrows + 127) / 128)), block(128);
   switch (a.D) {
-    case 32: hipLaunchKernelGGL((k_attn_simple<IN_T, 32>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_attn_simple<IN_T, 64>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_attn_simple<IN_T, 128>), grid, block, 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_attn_simple<32>), grid, block, 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_attn_simple<64>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_attn_simple<128>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -676,8 +703,14 @@ size_t attn_workspace_bytes(int dtype, int batch, int T, int Hq, int Hkv, int D,
 }
 
 hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
-  if (a.dtype == 1) return launch_simple<float>(a, st);
-  if (a.D != kD) return launch_simple<uint16_t>(a, st);
+  if (a.status) {
+    hipLaunchKernelGGL(k_zero_status, dim3((a.batch + 255) / 256), dim3(256), 0, st, a.status,
+                       a.batch);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // f32 (any D); bf16 is D = 128 only (checked by the caller)
+  if (a.dtype == 1) return launch_simple(a, st);
   const AttnSplit s = plan_split(a.dtype, a.batch, a.T, a.Hq, a.Hkv, a.D, a.max_prefix_len);
   float* part_o = nullptr;
   float* part_ml = nullptr;

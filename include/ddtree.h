@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define DDTREE_VERSION 10000 /* major * 10000 + minor * 100 + patch */
+#define DDTREE_VERSION 10100 /* major * 10000 + minor * 100 + patch */
 
 typedef enum { DDTREE_BF16 = 0, DDTREE_F32 = 1 } ddtree_dtype;
 
@@ -53,6 +53,11 @@ enum {
 /* Bits of status_flags[b] written by ddtree_build. */
 #define DDTREE_STATUS_NONFINITE 1   /* a NaN or +inf logit was ranked as -inf */
 #define DDTREE_STATUS_ALL_NEG_INF 2 /* a position had no finite logit         */
+/* Bits of status_flags[b] written by ddtree_verify_attn. */
+#define DDTREE_STATUS_OUT_NONFINITE 4 /* an output element of the request is not
+                                         finite (see ddtree_verify_attn)        */
+#define DDTREE_STATUS_BAD_KV 8        /* kv_offsets / prefix_lens outside the
+                                         caches: the request's rows are zeros   */
 
 /* Library version (DDTREE_VERSION of the build). Host only. */
 int ddtree_version(void);
@@ -132,17 +137,29 @@ int ddtree_mask(const int32_t *parents, const int32_t *num_nodes, int batch, int
  *                 are written as zeros
  *   mask          [batch, T, ceil(T/64)] uint64         in (layout of ddtree_build)
  *   max_prefix_len  an upper bound on every P_b (sizes the work split)
- *   total_rows    number of rows of k and v (bounds checking)
+ *   total_rows    number of rows of k and v
  *   softmax_scale <= 0 selects 1/sqrt(D)
+ *   status_flags  [batch] int32 or NULL                 out: DDTREE_STATUS_OUT_NONFINITE,
+ *                 DDTREE_STATUS_BAD_KV (0 when neither holds)
  *   workspace     >= ddtree_verify_workspace_size(...) bytes
+ *
+ * Request b's rows are checked on the device (the offsets and lengths may
+ * come from earlier kernels): kv_offsets[b] >= 0, P_b >= 0 and
+ * kv_offsets[b] + P_b + T <= total_rows. A request failing the check reads
+ * no key, its output rows are zeros and it gets DDTREE_STATUS_BAD_KV; this is
+ * not an error of the call.
  *
  * bf16: q.k on bf16 MFMA with fp32 accumulation; softmax in fp32; the
  * P.V product on fp16 MFMA (weights rounded to fp16, 2^-12 relative; V
- * converted to fp16, exact for |v| in [2^-14, 65504], values below that
- * range rounded to fp16 subnormals, values above it overflow); fp32
- * accumulation, bf16 output. f32: fp32 throughout.
- * Limits: Hq % Hkv == 0; T <= 1025; D in {32, 64, 128} (bf16: D = 128);
- * bf16 V within +-65504.
+ * converted to fp16, exact for |v| in [2^-14, 65280] -- the largest bf16
+ * value below the fp16 limit --, smaller values rounded to fp16 subnormals).
+ * A bf16 V value of magnitude 65536 or more (or a non-finite one) in the
+ * key tiles of a request becomes infinite in fp16 and makes that request's
+ * output rows non-finite; such a request gets DDTREE_STATUS_OUT_NONFINITE
+ * (as does any output row that is not finite, e.g. from fp32 score
+ * overflow). fp32 accumulation, bf16 output. f32: fp32 throughout, same
+ * status bits.
+ * Limits: Hq % Hkv == 0; T <= 1025; D in {32, 64, 128} (bf16: D = 128).
  */
 size_t ddtree_verify_workspace_size(ddtree_dtype dt, int batch, int T, int Hq, int Hkv, int D,
                                     int max_prefix_len);
@@ -150,8 +167,8 @@ int ddtree_verify_attn(const void *q, const void *k, const void *v, ddtree_dtype
                        const int64_t *kv_offsets, const int32_t *prefix_lens,
                        const int32_t *num_nodes, const uint64_t *mask, int batch, int T, int Hq,
                        int Hkv, int D, int max_prefix_len, int64_t total_rows,
-                       float softmax_scale, void *out, void *workspace, size_t workspace_bytes,
-                       void *stream);
+                       float softmax_scale, void *out, int32_t *status_flags, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /*
  * ddtree_accept -- greedy acceptance walk.                        [BDDT §4.1]
@@ -211,7 +228,9 @@ int ddtree_accept(const void *target_logits, ddtree_dtype dt, const int32_t *tar
  *   workspace       >= ddtree_accept_workspace_size(batch, T) bytes when
  *                   target_tokens is NULL (holds the sampled tokens); else
  *                   unused and may be NULL
- * Limits: T <= 1025, 1 <= L <= 64, 1 <= V <= 2^31 - 1.
+ * Limits: T <= 1025, 1 <= L <= 64, 1 <= V <= 2^19 (the fixed-point weights
+ * are below 2^45, so S stays below 2^64 exactly; DDTREE_ERR_UNSUPPORTED
+ * above).
  */
 int ddtree_accept_sample(const void *target_logits, ddtree_dtype dt, const int32_t *tokens,
                          const int32_t *parents, const int32_t *num_nodes, int batch, int T, int V,

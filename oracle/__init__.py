@@ -31,7 +31,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
              "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -53,6 +53,10 @@ def lib():
                      "oracle_argmax_rows", "oracle_walk", "oracle_accept",
                      "oracle_philox4x32_10", "oracle_accept_sample", "oracle_commit_kv"):
             getattr(L, name).restype = None
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_get_threads.restype = ctypes.c_int
+        L.oracle_get_threads.argtypes = []
         L.oracle_sample_row.restype = ctypes.c_int
         L.oracle_sample_row.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                         ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int]
@@ -62,6 +66,40 @@ def lib():
             [ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_int64] + [ctypes.c_void_p] * 2
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads for the batch-level calls (1 by default; results do not
+    depend on it)."""
+    lib().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().oracle_get_threads())
+
+
+def host_cores() -> int:
+    """CPU cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+class threads:
+    """Context manager: run the enclosed oracle calls on n threads."""
+
+    def __init__(self, n: int):
+        self.n = int(n)
+
+    def __enter__(self):
+        self.prev = get_threads()
+        set_threads(self.n)
+        return self
+
+    def __exit__(self, *exc):
+        set_threads(self.prev)
+        return False
 
 
 def _p(a: Optional[np.ndarray]):
@@ -170,7 +208,8 @@ def build_tree(logits, root_tokens, K: int, N: int, tau: float, want_mask: bool 
 
 def attn_rows(q, k, v, kv_offsets, prefix_lens, num_nodes, mask_words, T: int, Hq: int,
               Hkv: int, D: int, scale: float, sel):
-    """fp64 tree attention for the (b, i, h) triples in sel -> [len(sel), D]."""
+    """fp64 tree attention for the (b, i, h) triples in sel -> [len(sel), D].
+    The caches' row count is k's first dimension."""
     qr, dq = as_raw(q)
     kr, dk = as_raw(k)
     vr, dv = as_raw(v)
@@ -182,7 +221,8 @@ def attn_rows(q, k, v, kv_offsets, prefix_lens, num_nodes, mask_words, T: int, H
     s = _i32(sel).reshape(-1, 3)
     out = np.zeros((s.shape[0], D), np.float64)
     lib().oracle_attn_rows(_p(qr), _p(kr), _p(vr), dq, _p(offs), _p(pl), _p(nn), _p(mw), T, Hq,
-                           Hkv, D, ctypes.c_double(scale), _p(s), s.shape[0], _p(out))
+                           Hkv, D, ctypes.c_int64(kr.shape[0]), ctypes.c_double(scale), _p(s),
+                           s.shape[0], _p(out))
     return out
 
 

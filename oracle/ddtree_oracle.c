@@ -42,7 +42,13 @@
  *   lse   = fp32(LOG64(S * 2^-44))   LOG64: fp64 logarithm below
  *   lp_k  = fp32(d_{v_k} - lse)  for the K tokens ranked by (x desc, id asc)
  *
- * Build: gcc -O2 -std=c11 -ffp-contract=off (no fast-math).
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp (no fast-math).
+ *
+ * Threads: one by default. oracle_set_threads(n) lets the batch-level
+ * functions spread independent units over n OpenMP threads -- drafter rows
+ * and then requests (build), query rows (attention), target rows and then
+ * requests (accept) -- each unit computed by the same serial code, so the
+ * results do not depend on the thread count.
  */
 #include <math.h>
 #include <stddef.h>
@@ -52,6 +58,12 @@
 
 #define ODT_BF16 0
 #define ODT_F32 1
+
+static int g_threads = 1;
+
+void oracle_set_threads(int n) { g_threads = n > 0 ? n : 1; }
+
+int oracle_get_threads(void) { return g_threads; }
 
 static float load_value(const void *base, int dtype, size_t idx)
 {
@@ -348,15 +360,20 @@ void oracle_build(const void *logits, int dtype, const int32_t *root_tokens, int
     int T = N + 1;
     int W = (T + 63) / 64;
     size_t elem = (dtype == ODT_BF16) ? 2 : 4;
+    int rows = batch * L;
+    int *row_flags = (int *)malloc(sizeof(int) * (size_t)(rows > 0 ? rows : 1));
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
+    for (int r = 0; r < rows; ++r) {
+        const char *row = (const char *)logits + (size_t)r * (size_t)V * elem;
+        row_flags[r] = oracle_row_topk(row, dtype, V, K, tau, topk_tok + (size_t)r * K,
+                                       topk_lp + (size_t)r * K, row_m ? row_m + r : NULL,
+                                       row_S ? row_S + r : NULL, row_lse ? row_lse + r : NULL);
+    }
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
     for (int b = 0; b < batch; ++b) {
         int flags = 0;
-        for (int i = 0; i < L; ++i) {
-            size_t r = (size_t)b * L + i;
-            const char *row = (const char *)logits + r * (size_t)V * elem;
-            flags |= oracle_row_topk(row, dtype, V, K, tau, topk_tok + r * K, topk_lp + r * K,
-                                     row_m ? row_m + r : NULL, row_S ? row_S + r : NULL,
-                                     row_lse ? row_lse + r : NULL);
-        }
+        for (int i = 0; i < L; ++i)
+            flags |= row_flags[b * L + i];
         if (status)
             status[b] = flags;
         size_t o = (size_t)b * T;
@@ -366,6 +383,7 @@ void oracle_build(const void *logits, int dtype, const int32_t *root_tokens, int
         if (mask)
             oracle_mask(parents + o, num_nodes[b], T, mask + o * W);
     }
+    free(row_flags);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -375,22 +393,29 @@ void oracle_build(const void *logits, int dtype, const int32_t *root_tokens, int
 /* kv_offsets[b]: P_b prefix rows, then T tree rows in node order.           */
 /* Query (b, i, h) attends to every prefix row and to tree rows j whose mask */
 /* bit (i, j) is set; q-head h reads kv-head h / (Hq/Hkv). Rows i at or      */
-/* beyond num_nodes[b] are zero. Only the (b, i, h) triples in sel are       */
+/* beyond num_nodes[b] are zero, and so are all rows of a request whose K/V  */
+/* rows kv_offsets[b] .. kv_offsets[b] + P_b + T do not lie inside the      */
+/* total_rows rows of the caches. Only the (b, i, h) triples in sel are     */
 /* computed, into out[nsel, D].                                              */
 /* ------------------------------------------------------------------------ */
 void oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
                       const int64_t *kv_offsets, const int32_t *prefix_lens,
                       const int32_t *num_nodes, const uint64_t *mask, int T, int Hq, int Hkv,
-                      int D, double scale, const int32_t *sel, int nsel, double *out)
+                      int D, int64_t total_rows, double scale, const int32_t *sel, int nsel,
+                      double *out)
 {
     int g = Hq / Hkv;
     int W = (T + 63) / 64;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
     for (int s = 0; s < nsel; ++s) {
         int b = sel[3 * s], i = sel[3 * s + 1], h = sel[3 * s + 2];
         double *o = out + (size_t)s * D;
         for (int d = 0; d < D; ++d)
             o[d] = 0.0;
         if (i >= num_nodes[b])
+            continue;
+        if (kv_offsets[b] < 0 || prefix_lens[b] < 0 ||
+            kv_offsets[b] + prefix_lens[b] + T > total_rows)
             continue;
         int P = prefix_lens[b];
         int hk = h / g;
@@ -504,23 +529,24 @@ void oracle_accept(const void *target_logits, int dtype, const int32_t *target_i
                    int32_t *accept_len, int32_t *bonus, int32_t *target_argmax)
 {
     size_t elem = (dtype == ODT_BF16) ? 2 : 4;
-    int32_t *tgt = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
-    for (int b = 0; b < batch; ++b) {
-        for (int i = 0; i < T; ++i) {
-            if (i >= num_nodes[b]) {
-                tgt[i] = -1;
-            } else if (target_logits) {
-                const char *row =
-                    (const char *)target_logits + ((size_t)b * T + i) * (size_t)V * elem;
-                oracle_argmax_rows(row, dtype, 1, V, &tgt[i]);
-            } else {
-                tgt[i] = target_ids[(size_t)b * T + i];
-            }
-            if (target_argmax)
-                target_argmax[(size_t)b * T + i] = tgt[i];
+    int32_t *tgt = (int32_t *)malloc(sizeof(int32_t) * (size_t)batch * (size_t)T);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
+    for (int64_t r = 0; r < (int64_t)batch * T; ++r) {
+        int b = (int)(r / T), i = (int)(r % T);
+        if (i >= num_nodes[b]) {
+            tgt[r] = -1;
+        } else if (target_logits) {
+            const char *row = (const char *)target_logits + (size_t)r * (size_t)V * elem;
+            oracle_argmax_rows(row, dtype, 1, V, &tgt[r]);
+        } else {
+            tgt[r] = target_ids[r];
         }
+        if (target_argmax)
+            target_argmax[r] = tgt[r];
+    }
+    for (int b = 0; b < batch; ++b) {
         size_t o = (size_t)b * T;
-        oracle_walk(tokens + o, parents + o, num_nodes[b], tgt, L, accepted + (size_t)b * L,
+        oracle_walk(tokens + o, parents + o, num_nodes[b], tgt + o, L, accepted + (size_t)b * L,
                     accepted_nodes + (size_t)b * L, accept_len + b, bonus + b);
     }
     free(tgt);
@@ -613,21 +639,22 @@ void oracle_accept_sample(const void *target_logits, int dtype, const int32_t *t
                           int32_t *target_tokens)
 {
     size_t elem = (dtype == ODT_BF16) ? 2 : 4;
-    int32_t *tgt = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
-    for (int b = 0; b < batch; ++b) {
-        for (int i = 0; i < T; ++i) {
-            if (i >= num_nodes[b]) {
-                tgt[i] = -1;
-            } else {
-                const char *row =
-                    (const char *)target_logits + ((size_t)b * T + i) * (size_t)V * elem;
-                tgt[i] = oracle_sample_row(row, dtype, V, tau, seed, offset, b, i);
-            }
-            if (target_tokens)
-                target_tokens[(size_t)b * T + i] = tgt[i];
+    int32_t *tgt = (int32_t *)malloc(sizeof(int32_t) * (size_t)batch * (size_t)T);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
+    for (int64_t r = 0; r < (int64_t)batch * T; ++r) {
+        int b = (int)(r / T), i = (int)(r % T);
+        if (i >= num_nodes[b]) {
+            tgt[r] = -1;
+        } else {
+            const char *row = (const char *)target_logits + (size_t)r * (size_t)V * elem;
+            tgt[r] = oracle_sample_row(row, dtype, V, tau, seed, offset, b, i);
         }
+        if (target_tokens)
+            target_tokens[r] = tgt[r];
+    }
+    for (int b = 0; b < batch; ++b) {
         size_t o = (size_t)b * T;
-        oracle_walk(tokens + o, parents + o, num_nodes[b], tgt, L, accepted + (size_t)b * L,
+        oracle_walk(tokens + o, parents + o, num_nodes[b], tgt + o, L, accepted + (size_t)b * L,
                     accepted_nodes + (size_t)b * L, accept_len + b, bonus + b);
     }
     free(tgt);

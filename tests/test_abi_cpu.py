@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_strerror_and_sizes():
-    assert dtb.version() == 10000
+    assert dtb.version() == 10100
     for code in (OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP):
         assert dtb.strerror(code) and dtb.strerror(code) != "unknown status"
     assert dtb.strerror(-99) == "unknown status"
@@ -82,12 +82,12 @@ def test_build_rejects(kw, code):
 
 def _verify(**kw):
     a = dict(q=P, k=P, v=P, dt=0, offs=P, pl=P, nn=P, mask=P, batch=1, T=9, Hq=4, Hkv=2, D=128,
-             maxp=16, rows=100, scale=0.0, out=P, ws=P, wsb=1 << 24)
+             maxp=16, rows=100, scale=0.0, out=P, st=N0, ws=P, wsb=1 << 24)
     a.update(kw)
     return api.lib().ddtree_verify_attn(a["q"], a["k"], a["v"], a["dt"], a["offs"], a["pl"],
                                         a["nn"], a["mask"], a["batch"], a["T"], a["Hq"], a["Hkv"],
                                         a["D"], a["maxp"], a["rows"], a["scale"], a["out"],
-                                        a["ws"], a["wsb"], None)
+                                        a["st"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -136,7 +136,8 @@ def _sample(**kw):
     (dict(T=0), ERR_ARG), (dict(L=0), ERR_ARG), (dict(temp=0.0), ERR_ARG),
     (dict(temp=-0.5), ERR_ARG), (dict(temp=float("inf")), ERR_ARG),
     (dict(temp=float("nan")), ERR_ARG), (dict(dt=5), ERR_UNSUP), (dict(L=65), ERR_UNSUP),
-    (dict(T=1026), ERR_UNSUP), (dict(ws=N0), ERR_WS), (dict(wsb=8), ERR_WS),
+    (dict(T=1026), ERR_UNSUP), (dict(V=(1 << 19) + 1), ERR_UNSUP), (dict(V=(1 << 31) - 1), ERR_UNSUP),
+    (dict(ws=N0), ERR_WS), (dict(wsb=8), ERR_WS),
 ])
 def test_accept_sample_rejects(kw, code):
     _no_gpu()

@@ -1,13 +1,23 @@
 """GPU parity of ddtree_verify_attn against the oracle's fp64 tree attention.
 
 Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees",
-Abstract / §4.1 (one verify pass, ancestor-only mask), App. B. Tolerance:
-|gpu - ref| <= 1e-3 + 2e-2 |ref| for bf16 and 1e-5 + 1e-5 |ref| for f32.
+Abstract / §4.1 (one verify pass, ancestor-only mask), App. B (budgets up to
+1024). Tolerance: |gpu - ref| <= 1e-3 + 2e-2 |ref| for bf16 and
+1e-5 + 1e-5 |ref| for f32.
+
 Small shapes compare every output row (ragged prefixes straddling key tiles,
-trees with padding rows, GQA group sizes 1/4/8, row tiles with a ragged
-tail, the split-KV path with requests of different lengths and with fewer
-(request, kv-head) pairs than XCDs); the full-size workloads compare sampled rows in
-the launch configuration the benchmark times.
+trees with padding rows, GQA group sizes 1/4/8, row tiles with a ragged tail,
+the split-KV path with requests of different lengths and with fewer
+(request, kv-head) pairs than XCDs); the largest tree (T = 1025, split keys,
+ragged prefixes and a ragged last row tile) and a batch of more requests than
+XCDs compare every row as well. The full-size workloads run in the launch
+configuration the benchmark times and compare at least one row of every
+(request, kv-head, 128-row tile) unit of the kernel, every row of one query
+head per (request, kv-head) where the oracle's cost allows it (all but the
+65,536-key workload, which compares every row of one head for one kv-head
+per request), and each request's first, last and padding rows.
+Device-side checks: V values beyond the fp16 range and requests whose K/V
+rows are outside the caches are reported in the status words.
 """
 import numpy as np
 import pytest
@@ -19,6 +29,16 @@ from gpu_util import DEV, check_attn, note
 
 pytestmark = pytest.mark.gpu
 
+ROWS_PER_TILE = 128   # query rows of one attention workgroup
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _oracle_threads():
+    """The oracle's attention rows are spread over the host's cores (the
+    results do not depend on the thread count)."""
+    with oracle.threads(oracle.host_cores()):
+        yield
+
 
 def _tree(B, L, V, K, N, seed):
     g = torch.Generator().manual_seed(seed)
@@ -26,25 +46,41 @@ def _tree(B, L, V, K, N, seed):
     return oracle.build_tree(x, list(range(B)), K, N, 1.0)
 
 
-def _run(q, k, v, P, tree, T, max_prefix=None):
+def _run(q, k, v, P, tree, T, max_prefix=None, offs=None):
     B, _, Hq, D = q.shape
-    offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
-    mp = int(max(P)) if max_prefix is None else max_prefix
+    if offs is None:
+        offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
+    mp = int(max(max(P), 0)) if max_prefix is None else max_prefix
     code = 0 if q.dtype == torch.bfloat16 else 1
     ws = api.new_workspace(api.ddtree_verify_workspace_size(code, B, T, Hq, k.shape[1], D, mp), DEV)
     out = torch.full_like(q, 7.0, device=DEV)   # every row must be written
+    status = torch.full((B,), -1, dtype=torch.int32, device=DEV)   # every word must be written
     api.ddtree_verify_attn(q.to(DEV), k.to(DEV), v.to(DEV), offs.to(DEV),
                            torch.as_tensor(P, dtype=torch.int32).to(DEV),
                            torch.from_numpy(tree["num_nodes"]).to(DEV),
-                           torch.from_numpy(tree["mask"].view(np.int64)).to(DEV), mp, out, ws)
+                           torch.from_numpy(tree["mask"].view(np.int64)).to(DEV), mp, out, ws,
+                           status_flags=status)
     torch.cuda.synchronize()
-    return out.cpu(), offs
+    return out.cpu(), offs, status.cpu().numpy()
 
 
 def _ref(q, k, v, offs, P, tree, T, sel):
     Hq, Hkv, D = q.shape[2], k.shape[1], q.shape[3]
     return oracle.attn_rows(q, k, v, offs, P, tree["num_nodes"], tree["mask"], T, Hq, Hkv, D,
                             1.0 / np.sqrt(D), sel)
+
+
+def _qkv(B, T, Hq, Hkv, P, seed, dtype=torch.bfloat16, D=128):
+    g = torch.Generator().manual_seed(seed)
+    total = sum(P) + B * T
+    q = torch.randn(B, T, Hq, D, generator=g).to(dtype)
+    k = torch.randn(total, Hkv, D, generator=g).to(dtype)
+    v = torch.randn(total, Hkv, D, generator=g).to(dtype)
+    return q, k, v
+
+
+def _all_rows(B, T, Hq):
+    return [(b, i, h) for b in range(B) for i in range(T) for h in range(Hq)]
 
 
 SMALL = [
@@ -65,20 +101,52 @@ SMALL = [
 
 @pytest.mark.parametrize("B,L,V,K,N,Hq,Hkv,P", SMALL)
 def test_attn_bf16_all_rows(B, L, V, K, N, Hq, Hkv, P):
-    T, D = N + 1, 128
+    T = N + 1
     tree = _tree(B, L, V, K, N, seed=N + Hq)
-    g = torch.Generator().manual_seed(B * 1000 + N)
-    total = sum(P) + B * T
-    q = torch.randn(B, T, Hq, D, generator=g).to(torch.bfloat16)
-    k = torch.randn(total, Hkv, D, generator=g).to(torch.bfloat16)
-    v = torch.randn(total, Hkv, D, generator=g).to(torch.bfloat16)
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=B * 1000 + N)
     note("attn bf16 B=%d T=%d Hq=%d Hkv=%d P=%s" % (B, T, Hq, Hkv, P))
-    out, offs = _run(q, k, v, P, tree, T)
-    sel = [(b, i, h) for b in range(B) for i in range(T) for h in range(Hq)]
-    ref = _ref(q, k, v, offs, P, tree, T, sel)
-    check_attn(out, ref, sel, torch.bfloat16)
+    out, offs, st = _run(q, k, v, P, tree, T)
+    sel = _all_rows(B, T, Hq)
+    check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, torch.bfloat16)
     for b in range(B):
         assert torch.all(out[b, tree["num_nodes"][b]:] == 0)
+    assert np.all(st == 0), st
+
+
+def test_attn_bf16_largest_tree_all_rows():
+    """N = 1024 (T = 1025, 17 mask words): split keys, ragged prefixes that
+    straddle key tiles, 33 row tiles with a 4-row last tile."""
+    B, L, V, K, N, Hq, Hkv, P = 2, 16, 80, 8, 1024, 32, 8, [3001, 1703]
+    T = N + 1
+    tree = _tree(B, L, V, K, N, seed=1025)
+    assert int(tree["num_nodes"].min()) == T            # full trees
+    assert api.ddtree_verify_workspace_size(0, B, T, Hq, Hkv, 128, max(P)) > 256   # keys split
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=1025)
+    note("attn bf16 T=1025 all rows P=%s" % P)
+    out, offs, st = _run(q, k, v, P, tree, T)
+    sel = _all_rows(B, T, Hq)
+    check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, torch.bfloat16)
+    assert np.all(st == 0), st
+
+
+def test_attn_bf16_batch_beyond_xcds_all_rows():
+    """12 requests (more than the 8 XCDs the grid deals units to) with
+    unequal prefixes, some of them short of a key tile, and padded trees."""
+    B, L, V, K, N, Hq, Hkv = 12, 6, 40, 4, 64, 32, 8
+    T = N + 1
+    rng = np.random.default_rng(12)
+    P = [int(x) for x in rng.integers(0, 3000, size=B)]
+    P[3], P[7] = 0, 33
+    tree = _tree(B, L, V, K, N, seed=12)
+    tree["num_nodes"][5] = 17            # a short tree: rows 17.. are padding
+    tree["mask"][5, 17:] = 0
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=12)
+    note("attn bf16 B=12 all rows P=%s" % P)
+    out, offs, st = _run(q, k, v, P, tree, T)
+    sel = _all_rows(B, T, Hq)
+    check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, torch.bfloat16)
+    assert torch.all(out[5, 17:] == 0)
+    assert np.all(st == 0), st
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
@@ -86,35 +154,114 @@ def test_attn_f32_all_rows(D):
     B, L, V, K, N, Hq, Hkv, P = 2, 4, 30, 4, 8, 4, 2, [16, 3]
     T = N + 1
     tree = _tree(B, L, V, K, N, seed=D)
-    g = torch.Generator().manual_seed(D)
-    total = sum(P) + B * T
-    q = torch.randn(B, T, Hq, D, generator=g)
-    k = torch.randn(total, Hkv, D, generator=g)
-    v = torch.randn(total, Hkv, D, generator=g)
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=D, dtype=torch.float32, D=D)
     note("attn f32 D=%d" % D)
-    out, offs = _run(q, k, v, P, tree, T)
-    sel = [(b, i, h) for b in range(B) for i in range(T) for h in range(Hq)]
+    out, offs, st = _run(q, k, v, P, tree, T)
+    sel = _all_rows(B, T, Hq)
     check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, torch.float32)
+    assert np.all(st == 0), st
 
 
 def test_attn_repeatable_split_counters():
     """Two split-KV calls on one workspace give identical bits (partials rewritten)."""
     B, L, V, K, N, Hq, Hkv, P = 1, 16, 80, 8, 64, 32, 8, [3000]
-    T, D = N + 1, 128
+    T = N + 1
     tree = _tree(B, L, V, K, N, seed=1)
-    g = torch.Generator().manual_seed(2)
-    total = sum(P) + B * T
-    q = torch.randn(B, T, Hq, D, generator=g).to(torch.bfloat16)
-    k = torch.randn(total, Hkv, D, generator=g).to(torch.bfloat16)
-    v = torch.randn(total, Hkv, D, generator=g).to(torch.bfloat16)
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=2)
     note("attn split twice")
-    a, _ = _run(q, k, v, P, tree, T)
-    b, _ = _run(q, k, v, P, tree, T)
+    a, _, _ = _run(q, k, v, P, tree, T)
+    b, _, _ = _run(q, k, v, P, tree, T)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("P", [[2048, 700], [100, 40]])   # split keys / one split
+def test_attn_v_range_status(P):
+    """bf16 V enters the P.V product as fp16: 65280 (the largest bf16 value
+    below the fp16 limit) is exact and matches the oracle; 65536 (which is
+    where 65504 rounds in bf16) and 1e5 overflow fp16, and the request that
+    holds them is flagged DDTREE_STATUS_OUT_NONFINITE while the other
+    request's rows still match."""
+    B, L, V, K, N, Hq, Hkv = 2, 4, 30, 4, 20, 32, 8
+    T = N + 1
+    tree = _tree(B, L, V, K, N, seed=5)
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=5)
+    offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
+    v[int(offs[0]) + 3, 2, 7] = 65280.0                  # request 0: in range
+    v[int(offs[0]) + P[0] + 1, 5, 100] = -65280.0        # (a tree row, node 1)
+    note("attn V range: in range P=%s" % P)
+    out, _, st = _run(q, k, v, P, tree, T)
+    sel = _all_rows(B, T, Hq)
+    check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, torch.bfloat16)
+    assert np.all(st == 0), st
+    for big in (65504.0, 1e5):
+        v2 = v.clone()
+        v2[int(offs[1]) + 1, 0, 0] = big                 # request 1, a prefix row of kv-head 0
+        assert abs(float(v2[int(offs[1]) + 1, 0, 0])) >= 65536
+        note("attn V range: %g P=%s" % (big, P))
+        out, _, st = _run(q, k, v2, P, tree, T)
+        assert st[0] == 0 and st[1] == api.STATUS_OUT_NONFINITE, st
+        sel0 = _all_rows(1, T, Hq)
+        check_attn(out, _ref(q, k, v2, offs, P, tree, T, sel0), sel0, torch.bfloat16)
+
+
+def test_attn_bad_kv_rows_zero_and_flagged():
+    """Requests whose K/V rows are not inside the caches (a negative offset, a
+    negative prefix, a region past the last row) read nothing: their rows are
+    zeros and DDTREE_STATUS_BAD_KV is set; the valid request matches. Every
+    buffer is in bounds: the device check keeps the kernel from reading the
+    described rows at all."""
+    B, L, V, K, N, Hq, Hkv = 4, 4, 30, 4, 20, 32, 8
+    T = N + 1
+    P = [300, 300, 300, 300]
+    tree = _tree(B, L, V, K, N, seed=6)
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=6)
+    total = k.shape[0]
+    offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
+    P_bad = list(P)
+    offs[0] = -5                     # negative offset
+    P_bad[2] = -1                    # negative prefix
+    offs[3] = total - P[3] - T + 1   # one row past the caches
+    for dtype in (torch.bfloat16, torch.float32):
+        note("attn bad kv rows dtype=%s" % dtype)
+        qq, kk, vv = (t.to(dtype) for t in (q, k, v))
+        out, _, st = _run(qq, kk, vv, P_bad, tree, T, max_prefix=max(P), offs=offs)
+        assert list(st) == [api.STATUS_BAD_KV, 0, api.STATUS_BAD_KV, api.STATUS_BAD_KV], st
+        for b in (0, 2, 3):
+            assert torch.all(out[b] == 0)
+        sel = [(1, i, h) for i in range(T) for h in range(Hq)]
+        ref = _ref(qq, kk, vv, offs, P_bad, tree, T, sel)
+        check_attn(out, ref, sel, dtype)
+        # the oracle reads the same rule: the bad requests' rows are zeros
+        sel_bad = [(b, i, 3) for b in (0, 2, 3) for i in (0, T - 1)]
+        assert np.all(_ref(qq, kk, vv, offs, P_bad, tree, T, sel_bad) == 0)
+
+
+def _unit_rows(w, tree, rng):
+    """At least one row of every (request, kv-head, 128-row tile) unit, and
+    the first, last and (when present) first padding row of every request."""
+    g = w.Hq // w.Hkv
+    R = w.T * g
+    sel = []
+    for b in range(w.batch):
+        nn = int(tree["num_nodes"][b])
+        for hk in range(w.Hkv):
+            for t0 in range(0, R, ROWS_PER_TILE):
+                r = int(rng.integers(t0, min(t0 + ROWS_PER_TILE, R)))
+                node, j = divmod(r, g)
+                sel.append((b, node, hk * g + j))
+        for i in sorted({0, nn - 1} | ({nn} if nn < w.T else set())):
+            sel += [(b, i, 0), (b, i, w.Hq - 1)]
+    return sel
+
+
+def _head_rows(w, tree, pairs):
+    """Every node's row of one query head for each (request, kv-head) pair."""
+    g = w.Hq // w.Hkv
+    return [(b, i, hk * g + (b + hk) % g) for (b, hk) in pairs for i in range(w.T)]
+
+
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
-def test_attn_full_size_workloads_sampled(name):
+def test_attn_full_size_workloads(name):
     w = synth.WORKLOADS[name]
     x, _ = synth.drafter_logits(w)
     roots = synth.root_tokens(w)
@@ -122,11 +269,17 @@ def test_attn_full_size_workloads_sampled(name):
     P = synth.prefix_lengths(w)
     q, k, v = synth.qkv(w, P)
     note("attn workload %s rows=%d" % (name, k.shape[0]))
-    out, offs = _run(q, k, v, P.numpy(), tree, w.T, max_prefix=w.prefix[1])
+    out, offs, st = _run(q, k, v, P.numpy(), tree, w.T, max_prefix=w.prefix[1])
+    assert np.all(st == 0), st
     rng = np.random.default_rng(0)
-    nsamp = 4096 if w.prefix[1] <= 2048 else 384
-    sel = [(int(rng.integers(w.batch)), int(rng.integers(w.T)), int(rng.integers(w.Hq)))
-           for _ in range(nsamp)]
-    sel += [(b, int(tree["num_nodes"][b]) - 1, w.Hq - 1) for b in range(w.batch)]
+    if w.prefix[1] <= 2048:       # small: every row
+        sel = _all_rows(w.batch, w.T, w.Hq)
+    else:
+        sel = _unit_rows(w, tree, rng)
+        if w.prefix[1] < 65536:
+            pairs = [(b, hk) for b in range(w.batch) for hk in range(w.Hkv)]
+        else:
+            pairs = [(b, (3 * b + 1) % w.Hkv) for b in range(w.batch)]
+        sel += _head_rows(w, tree, pairs)
     ref = _ref(q, k, v, offs, P.numpy(), tree, w.T, sel)
     check_attn(out, ref, sel, q.dtype)
