@@ -49,6 +49,9 @@ def lib():
         L.ddtree_build.restype = i32
         L.ddtree_build.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                    vp, vp, vp, vp, vp, sz, vp]
+        L.ddtree_build_noalloc.restype = i32
+        L.ddtree_build_noalloc.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                           vp, vp, vp, vp, vp, vp, vp]
         L.ddtree_mask.restype = i32
         L.ddtree_mask.argtypes = [vp, vp, i32, i32, vp, vp]
         L.ddtree_verify_workspace_size.restype = sz
@@ -145,6 +148,22 @@ def ddtree_build(logits: torch.Tensor, root_tokens: torch.Tensor, K: int, N: int
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream, logits.device))
     _check("ddtree_build", code)
+
+
+def ddtree_build_noalloc(logits: torch.Tensor, root_tokens: torch.Tensor, K: int, N: int,
+                         draft_temp: float, tokens: torch.Tensor, parents: torch.Tensor,
+                         depths: torch.Tensor, scores: torch.Tensor, num_nodes: torch.Tensor,
+                         mask: Optional[torch.Tensor], topk_tokens: Optional[torch.Tensor],
+                         topk_logprobs: Optional[torch.Tensor],
+                         status_flags: Optional[torch.Tensor], stream=None) -> None:
+    """ddtree_build with the library's static scratch instead of a workspace."""
+    batch, L, V = logits.shape
+    code = lib().ddtree_build_noalloc(
+        _ptr(logits), _dtype_code(logits), _ptr(root_tokens), batch, L, V, K, N,
+        float(draft_temp), _ptr(tokens), _ptr(parents), _ptr(depths), _ptr(scores),
+        _ptr(num_nodes), _ptr(mask), _ptr(topk_tokens), _ptr(topk_logprobs), _ptr(status_flags),
+        _stream(stream, logits.device))
+    _check("ddtree_build_noalloc", code)
 
 
 def ddtree_mask(parents: torch.Tensor, num_nodes: torch.Tensor, mask: torch.Tensor,

@@ -4,16 +4,44 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/ddtree.h"
 #include "ddtree_internal.h"
 
 using namespace ddt;
+
+// Build scratch of ddtree_build_noalloc: one copy per GPU, alive until the
+// process ends. Host code never uses this name as an address (on the host it
+// is a stand-in, not device memory): it takes the device address from
+// hipGetSymbolAddress, per device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[DDTREE_BUILD_SCRATCH_MAX];
 
 namespace {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP; }
 
 inline bool dtype_ok(int dt) { return dt == DDTREE_BF16 || dt == DDTREE_F32; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device: looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DDTREE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DDTREE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DDTREE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DDTREE_OK;
+}
 
 }  // namespace
 
@@ -28,6 +56,8 @@ const char* ddtree_strerror(int status) {
     case DDTREE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
     case DDTREE_ERR_WORKSPACE: return "workspace missing or too small";
     case DDTREE_ERR_HIP: return "HIP launch failed";
+    case DDTREE_ERR_SCRATCH:
+      return "shape needs more build scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -38,11 +68,14 @@ size_t ddtree_build_workspace_size(int batch, int L, int V, int K, int N) {
   return build_workspace_bytes(batch, L, V, K);
 }
 
-int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens, int batch,
-                 int L, int V, int K, int N, float draft_temp, int32_t* tokens,
-                 int32_t* parents, int32_t* depths, float* scores, int32_t* num_nodes,
-                 uint64_t* mask, int32_t* topk_tokens, float* topk_logprobs,
-                 int32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of ddtree_build other than the workspace (host only).
+int build_check(const void* logits, int dt, const int32_t* root_tokens, int batch, int L, int V,
+                int K, int N, float draft_temp, const int32_t* tokens, const int32_t* parents,
+                const int32_t* depths, const float* scores, const int32_t* num_nodes) {
   if (!logits || !root_tokens || !tokens || !parents || !depths || !scores || !num_nodes)
     return DDTREE_ERR_ARG;
   if (batch < 1 || L < 1 || V < 1 || K < 1 || N < 1) return DDTREE_ERR_ARG;
@@ -52,9 +85,14 @@ int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens
   if (L > DDTREE_MAX_L || K > DDTREE_MAX_K || N > DDTREE_MAX_N || V > DDTREE_MAX_V)
     return DDTREE_ERR_UNSUPPORTED;
   if ((long long)batch * L > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
-  const size_t need = build_workspace_bytes(batch, L, V, K);
-  if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
+  return DDTREE_OK;
+}
 
+int build_launch(const void* logits, int dt, const int32_t* root_tokens, int batch, int L, int V,
+                 int K, int N, float draft_temp, int32_t* tokens, int32_t* parents,
+                 int32_t* depths, float* scores, int32_t* num_nodes, uint64_t* mask,
+                 int32_t* topk_tokens, float* topk_logprobs, int32_t* status_flags,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   BuildArgs a{};
   a.logits = logits;
   a.dtype = dt;
@@ -81,6 +119,43 @@ int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens
   a.topk_tok = topk_tokens;
   a.topk_lp = topk_logprobs;
   return hip_status(launch_build(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens, int batch,
+                 int L, int V, int K, int N, float draft_temp, int32_t* tokens,
+                 int32_t* parents, int32_t* depths, float* scores, int32_t* num_nodes,
+                 uint64_t* mask, int32_t* topk_tokens, float* topk_logprobs,
+                 int32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  const int chk = build_check(logits, dt, root_tokens, batch, L, V, K, N, draft_temp, tokens,
+                              parents, depths, scores, num_nodes);
+  if (chk != DDTREE_OK) return chk;
+  const size_t need = build_workspace_bytes(batch, L, V, K);
+  if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
+  return build_launch(logits, dt, root_tokens, batch, L, V, K, N, draft_temp, tokens, parents,
+                      depths, scores, num_nodes, mask, topk_tokens, topk_logprobs, status_flags,
+                      workspace, workspace_bytes, stream);
+}
+
+int ddtree_build_noalloc(const void* logits, ddtree_dtype dt, const int32_t* root_tokens,
+                         int batch, int L, int V, int K, int N, float draft_temp,
+                         int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
+                         int32_t* num_nodes, uint64_t* mask, int32_t* topk_tokens,
+                         float* topk_logprobs, int32_t* status_flags, void* stream) {
+  const int chk = build_check(logits, dt, root_tokens, batch, L, V, K, N, draft_temp, tokens,
+                              parents, depths, scores, num_nodes);
+  if (chk != DDTREE_OK) return chk;
+  if (build_workspace_bytes(batch, L, V, K) > (size_t)DDTREE_BUILD_SCRATCH_MAX)
+    return DDTREE_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != DDTREE_OK) return st;
+  return build_launch(logits, dt, root_tokens, batch, L, V, K, N, draft_temp, tokens, parents,
+                      depths, scores, num_nodes, mask, topk_tokens, topk_logprobs, status_flags,
+                      ws, (size_t)DDTREE_BUILD_SCRATCH_MAX, stream);
 }
 
 int ddtree_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int T,

@@ -41,7 +41,9 @@ enum {
     DDTREE_ERR_ARG = -1,         /* null pointer, size or range violation   */
     DDTREE_ERR_UNSUPPORTED = -2, /* dtype / shape outside the limits below  */
     DDTREE_ERR_WORKSPACE = -3,   /* workspace pointer missing or too small  */
-    DDTREE_ERR_HIP = -4          /* a HIP launch failed                     */
+    DDTREE_ERR_HIP = -4,         /* a HIP launch failed                     */
+    DDTREE_ERR_SCRATCH = -5      /* ddtree_build_noalloc: the shape needs more
+                                    scratch than DDTREE_BUILD_SCRATCH_MAX    */
 };
 
 /* Limits. */
@@ -106,6 +108,32 @@ int ddtree_build(const void *logits, ddtree_dtype dt, const int32_t *root_tokens
                  int32_t *parents, int32_t *depths, float *scores, int32_t *num_nodes,
                  uint64_t *mask, int32_t *topk_tokens, float *topk_logprobs,
                  int32_t *status_flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ddtree_build_noalloc -- ddtree_build without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, outputs, limits and return codes as ddtree_build, minus
+ * the workspace. The scratch the build kernels need (per-row candidate
+ * words, fixed-point sums, row maxima and flags) lives in a static device
+ * array of DDTREE_BUILD_SCRATCH_MAX bytes inside the library: one copy per
+ * GPU, kept until the process ends. No call allocates or frees anything.
+ * A shape whose scratch, ddtree_build_workspace_size(batch, L, V, K, N),
+ * exceeds DDTREE_BUILD_SCRATCH_MAX is rejected with DDTREE_ERR_SCRATCH
+ * before anything is enqueued (the workloads of this library need at most
+ * 0.8 MiB: e.g. 32 requests x 16 positions x V = 151936, K = 8).
+ * Every call on one GPU uses that GPU's one array, whatever the stream: calls
+ * that overlap on one GPU (concurrent streams or host threads) race, so
+ * callers serialise them. No contents carry from one call to the next (the
+ * kernels write every scratch word before reading it).
+ */
+#define DDTREE_BUILD_SCRATCH_MAX (4 << 20)
+int ddtree_build_noalloc(const void *logits, ddtree_dtype dt, const int32_t *root_tokens,
+                         int batch, int L, int V, int K, int N, float draft_temp,
+                         int32_t *tokens, int32_t *parents, int32_t *depths, float *scores,
+                         int32_t *num_nodes, uint64_t *mask, int32_t *topk_tokens,
+                         float *topk_logprobs, int32_t *status_flags, void *stream);
 
 /*
  * ddtree_mask -- ancestor-only attention bitmask of given trees.

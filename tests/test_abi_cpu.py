@@ -13,7 +13,7 @@ from draft_tree_build_amd import api
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ddtree.h")
 
-OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 
 
 def _declared():
@@ -24,7 +24,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     L = ctypes.CDLL(api.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_strerror_and_sizes():
     assert dtb.version() == 10100
-    for code in (OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP):
+    for code in (OK, ERR_ARG, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_SCRATCH):
         assert dtb.strerror(code) and dtb.strerror(code) != "unknown status"
     assert dtb.strerror(-99) == "unknown status"
     assert dtb.ddtree_build_workspace_size(32, 16, 151936, 8, 128) >= 32 * 16 * 8 * 8
@@ -78,6 +78,32 @@ def _build(**kw):
 def test_build_rejects(kw, code):
     _no_gpu()
     assert _build(**kw) == code
+
+
+def _build_noalloc(**kw):
+    a = dict(logits=P, dt=0, root=P, batch=2, L=4, V=64, K=4, N=8, temp=1.0, tokens=P, parents=P,
+             depths=P, scores=P, nn=P, mask=N0, tk=N0, tl=N0, st=N0)
+    a.update(kw)
+    return api.lib().ddtree_build_noalloc(a["logits"], a["dt"], a["root"], a["batch"], a["L"],
+                                          a["V"], a["K"], a["N"], a["temp"], a["tokens"],
+                                          a["parents"], a["depths"], a["scores"], a["nn"],
+                                          a["mask"], a["tk"], a["tl"], a["st"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=N0), ERR_ARG), (dict(nn=N0), ERR_ARG), (dict(N=0), ERR_ARG),
+    (dict(temp=float("nan")), ERR_ARG), (dict(dt=7), ERR_UNSUP), (dict(K=33, V=100), ERR_UNSUP),
+    (dict(V=(1 << 19) + 1), ERR_UNSUP),
+    # scratch beyond the static buffer (6.5 MB for 256 x 16 rows of 151936): rejected
+    (dict(batch=256, L=16, V=151936, K=8, N=128), ERR_SCRATCH),
+])
+def test_build_noalloc_rejects(kw, code):
+    """Same argument checks as ddtree_build, then the scratch limit; all on
+    the host before any HIP call."""
+    _no_gpu()
+    assert _build_noalloc(**kw) == code
+    need = dtb.ddtree_build_workspace_size(256, 16, 151936, 8, 128)
+    assert need > 4 << 20 >= dtb.ddtree_build_workspace_size(32, 16, 151936, 8, 128)
 
 
 def _verify(**kw):
