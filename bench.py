@@ -18,6 +18,9 @@ default workload's inputs, 1.8 GB per step, exceed it with one copy).
 Every timed step replays each stage's captured HIP graph with HIP events
 between the stages on the stream the kernels run on, so every stage of
 every timed step is event-timed (mean, median, p10, p90 in the JSON line).
+With --graph-mode round (small workloads, whose stages are short enough for
+host launch time to show between them), one graph holds the whole round and
+every 20th timed step runs the stages eagerly with the events between them.
 
 Prints one JSON line. value = sum over requests of (num_nodes - 1) per step
 divided by the time per step. The CPU baseline is the oracle, timed on one
@@ -323,16 +326,21 @@ def measure(w, args, dev):
     # the first and after each: the events time every stage of every timed
     # step on the stream the kernels run on. --no-graphs launches the ABI
     # calls directly instead, with the same events.
+    # --graph-mode round (small workloads, where host launch time would
+    # show between stages): one graph per copy holds the whole round; every
+    # 20th timed step instead calls the ABI functions directly with the
+    # events between them (the replays queued ahead keep the GPU busy).
     graphs = None
+    per_stage = args.graphs and args.graph_mode == "stage"
     if args.graphs:
-        log("capturing %d x %d graphs" % (R, len(stages)))
+        log("capturing %d x %d graph(s)" % (R, len(stages) if per_stage else 1))
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         graphs = []
         with torch.cuda.stream(side):
             for c in range(R):
                 row = []
-                for f in stages:
+                for f in (stages if per_stage else (lambda cc: [g(cc) for g in stages],)):
                     g = torch.cuda.CUDAGraph()
                     with torch.cuda.graph(g, stream=side):
                         f(copies[c])
@@ -344,17 +352,21 @@ def measure(w, args, dev):
                 g.replay()
         torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-           for _ in range(args.steps)]
-    log("timing %d steps (stage events on every step)" % args.steps)
+    every = 1 if (graphs is None or per_stage) else 20
+    timed = [i for i in range(args.steps) if i % every == every - 1] or [args.steps - 1]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for i in timed}
+    log("timing %d steps (stage events on %d)" % (args.steps, len(timed)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         c = i % R
-        ev = evs[i]
+        ev = evs.get(i)
+        if ev is None:
+            graphs[c][0].replay()
+            continue
         ev[0].record()
         for k in range(len(stages)):
-            if graphs is not None:
+            if per_stage:
                 graphs[c][k].replay()
             else:
                 stages[k](copies[c])
@@ -362,9 +374,9 @@ def measure(w, args, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_samples = {name: [evs[i][k].elapsed_time(evs[i][k + 1]) * 1e3 for i in range(args.steps)]
+    stage_samples = {name: [evs[i][k].elapsed_time(evs[i][k + 1]) * 1e3 for i in timed]
                      for k, name in enumerate(stage_names)}
-    step_samples = [evs[i][0].elapsed_time(evs[i][-1]) * 1e3 for i in range(args.steps)]
+    step_samples = [evs[i][0].elapsed_time(evs[i][-1]) * 1e3 for i in timed]
     stage_us = {k: sum(v) / len(v) for k, v in stage_samples.items()}
     value = nodes_per_step / (ms_per_step * 1e-3)
     log("ms/step %.4f  stages(us, mean) %s" % (ms_per_step, {k: round(v, 2) for k, v in stage_us.items()}))
@@ -394,7 +406,8 @@ def budget_sweep(w, args, dev, budgets):
            "dtype": w.dtype, "data": "synthetic (seeded)",
            "config": {"workload": w.name, "batch": w.batch, "L": w.L, "V": w.V, "K": w.K,
                       "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                      "target_temp": args.target_temp, "hip_graphs": bool(args.graphs)},
+                      "target_temp": args.target_temp, "hip_graphs": bool(args.graphs),
+                      "graph_mode": args.graph_mode},
            "sweep": recs}
     print(json.dumps(out), flush=True)
 
@@ -494,6 +507,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", dest="graphs", action="store_false",
                     help="launch the ABI calls eagerly instead of replaying captured HIP graphs")
+    ap.add_argument("--graph-mode", choices=("stage", "round"), default="stage",
+                    help="stage: one graph per stage, events between stages on every timed step; "
+                         "round: one graph per round (no host time between stages; for small "
+                         "workloads), every 20th timed step event-timed per stage")
     ap.add_argument("--target-temp", type=float, default=0.0,
                     help="target temperature of the acceptance (0: greedy arg-max; > 0: "
                          "ddtree_accept_sample)")
@@ -600,7 +617,8 @@ def main():
                    "prefix": list(w.prefix), "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "draft_temp": tau, "target_temp": args.target_temp,
                    "commit_kv": bool(args.commit_kv), "input_copies": R,
-                   "hip_graphs": bool(args.graphs), "stage_event_steps": args.steps,
+                   "hip_graphs": bool(args.graphs), "graph_mode": args.graph_mode,
+                   "stage_event_steps": m.stage_stats["build"]["n"],
                    "cache": "cold" if R > 1 or m.step_bytes > LLC_BYTES else "warm",
                    "step_input_MB": round(m.step_bytes / 1e6, 1)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},

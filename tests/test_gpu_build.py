@@ -233,3 +233,51 @@ def test_build_many_tied_candidates(B, L, V, K, frac):
         gb, _ = gpu_build(x, roots, K, 40, tau)
         o = oracle.build_tree(x, roots, K, 40, tau)
         assert_same_build(gb, o)
+
+
+def _few_values(B, L, V, seed, values):
+    """Logits drawn from a handful of values: log-probabilities tie within
+    rows, so scores tie across siblings, cousins and depths."""
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.randint(0, len(values), (B, L, V), generator=g)
+    return torch.tensor(values, dtype=torch.float32)[idx].to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("L,V,K,N,kind", [
+    (8, 500, 8, 129, "normal"), (16, 4000, 16, 300, "normal"), (32, 3000, 16, 1024, "normal"),
+    (6, 400, 12, 500, "few"), (16, 600, 16, 1024, "few"), (3, 50, 32, 1024, "few"),
+    (64, 300, 2, 1000, "few"), (4, 40, 4, 1024, "normal"),   # budget above the restricted set (340)
+    (40, 300, 1, 200, "normal"), (12, 700, 8, 257, "peaked"),
+])
+@pytest.mark.parametrize("tau", [1.0, 0.7, 0.0])
+def test_build_level_selection(L, V, K, N, kind, tau):
+    """Budgets above 128 run the level-synchronous selection: ties at the
+    threshold score (bf16 logits from a handful of values, temperature 0's
+    -inf tails), budgets above the restricted set (padding rows), K = 1
+    chains, deep trees under a peaked drafter."""
+    B = 2
+    if kind == "few":
+        x = _few_values(B, L, V, seed=L * V + N, values=[2.0, 1.0, 1.0, 0.5, 0.0, -1.0])
+    elif kind == "peaked":
+        x = _logits(B, L, V, seed=L + N, sigma=1.0, boost=12.0)
+    else:
+        x = _logits(B, L, V, seed=L + N + K, sigma=2.0)
+    roots = [3, 4]
+    note("build level L=%d V=%d K=%d N=%d %s tau=%g" % (L, V, K, N, kind, tau))
+    g, _ = gpu_build(x, roots, K, N, tau)
+    o = oracle.build_tree(x, roots, K, N, tau)
+    assert_same_build(g, o)
+
+
+@pytest.mark.parametrize("value", [0.0, float("-inf")])
+def test_build_level_selection_degenerate_rows(value):
+    """All-equal rows (every prefix of a depth ties) and rows that are -inf
+    past position 0 (scores -inf below depth 1), at budgets above 128."""
+    B, L, V, K, N = 2, 6, 300, 8, 600
+    x = torch.full((B, L, V), value, dtype=torch.bfloat16)
+    x[:, 0, :] = torch.linspace(0, 3, V).to(torch.bfloat16)
+    for tau in (1.0, 0.0):
+        note("build level degenerate value=%g tau=%g" % (value, tau))
+        g, _ = gpu_build(x, [1, 2], K, N, tau)
+        o = oracle.build_tree(x, [1, 2], K, N, tau)
+        assert_same_build(g, o)
