@@ -3,6 +3,7 @@
 // anything is enqueued, so a rejected call has no effect on the device.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -22,6 +23,23 @@ namespace {
 inline int hip_status(hipError_t e) { return e == hipSuccess ? DDTREE_OK : DDTREE_ERR_HIP; }
 
 inline bool dtype_ok(int dt) { return dt == DDTREE_BF16 || dt == DDTREE_F32; }
+
+// The dtype argument as an int. C callers (and foreign-function bindings) may
+// pass any int in the enum's place; the bytes are read as an int, so a value
+// outside the enumerators is rejected rather than loaded as an enum.
+inline int dtype_value(const ddtree_dtype* d) {
+  int v;
+  static_assert(sizeof(v) == sizeof(*d), "enum and int differ in size");
+  memcpy(&v, d, sizeof v);
+  return v;
+}
+
+// a * b * c <= 2^31 - 1 for positive a, b, c, decided without forming a
+// product that could overflow
+inline bool product_fits_i32(long long a, long long b, long long c = 1) {
+  const long long lim = 0x7FFFFFFFLL;
+  return a <= lim / b && a * b <= lim / c;
+}
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -64,7 +82,9 @@ const char* ddtree_strerror(int status) {
 
 size_t ddtree_build_workspace_size(int batch, int L, int V, int K, int N) {
   (void)N;
-  if (batch < 1 || L < 1 || K < 1 || V < 1 || K > DDTREE_MAX_K) return 0;
+  if (batch < 1 || L < 1 || K < 1 || V < 1) return 0;
+  if (L > DDTREE_MAX_L || K > DDTREE_MAX_K || V > DDTREE_MAX_V) return 0;
+  if (!product_fits_i32(batch, L)) return 0;
   return build_workspace_bytes(batch, L, V, K);
 }
 
@@ -84,7 +104,7 @@ int build_check(const void* logits, int dt, const int32_t* root_tokens, int batc
   if (!dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
   if (L > DDTREE_MAX_L || K > DDTREE_MAX_K || N > DDTREE_MAX_N || V > DDTREE_MAX_V)
     return DDTREE_ERR_UNSUPPORTED;
-  if ((long long)batch * L > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  if (!product_fits_i32(batch, L)) return DDTREE_ERR_UNSUPPORTED;
   return DDTREE_OK;
 }
 
@@ -125,11 +145,12 @@ int build_launch(const void* logits, int dt, const int32_t* root_tokens, int bat
 
 extern "C" {
 
-int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens, int batch,
+int ddtree_build(const void* logits, ddtree_dtype dt_arg, const int32_t* root_tokens, int batch,
                  int L, int V, int K, int N, float draft_temp, int32_t* tokens,
                  int32_t* parents, int32_t* depths, float* scores, int32_t* num_nodes,
                  uint64_t* mask, int32_t* topk_tokens, float* topk_logprobs,
                  int32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  const int dt = dtype_value(&dt_arg);
   const int chk = build_check(logits, dt, root_tokens, batch, L, V, K, N, draft_temp, tokens,
                               parents, depths, scores, num_nodes);
   if (chk != DDTREE_OK) return chk;
@@ -140,11 +161,12 @@ int ddtree_build(const void* logits, ddtree_dtype dt, const int32_t* root_tokens
                       workspace, workspace_bytes, stream);
 }
 
-int ddtree_build_noalloc(const void* logits, ddtree_dtype dt, const int32_t* root_tokens,
+int ddtree_build_noalloc(const void* logits, ddtree_dtype dt_arg, const int32_t* root_tokens,
                          int batch, int L, int V, int K, int N, float draft_temp,
                          int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
                          int32_t* num_nodes, uint64_t* mask, int32_t* topk_tokens,
                          float* topk_logprobs, int32_t* status_flags, void* stream) {
+  const int dt = dtype_value(&dt_arg);
   const int chk = build_check(logits, dt, root_tokens, batch, L, V, K, N, draft_temp, tokens,
                               parents, depths, scores, num_nodes);
   if (chk != DDTREE_OK) return chk;
@@ -167,19 +189,24 @@ int ddtree_mask(const int32_t* parents, const int32_t* num_nodes, int batch, int
                                 static_cast<hipStream_t>(stream)));
 }
 
-size_t ddtree_verify_workspace_size(ddtree_dtype dt, int batch, int T, int Hq, int Hkv, int D,
+size_t ddtree_verify_workspace_size(ddtree_dtype dt_arg, int batch, int T, int Hq, int Hkv, int D,
                                     int max_prefix_len) {
+  const int dt = dtype_value(&dt_arg);
   if (batch < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_prefix_len < 0) return 0;
-  if (Hq % Hkv != 0) return 0;
+  if (Hq % Hkv != 0 || !dtype_ok(dt) || T > DDTREE_MAX_N + 1) return 0;
+  if (D != 32 && D != 64 && D != 128) return 0;
+  if (dt == DDTREE_BF16 && D != 128) return 0;
+  if (!product_fits_i32(batch, T, Hq)) return 0;
   return attn_workspace_bytes(dt, batch, T, Hq, Hkv, D, max_prefix_len);
 }
 
-int ddtree_verify_attn(const void* q, const void* k, const void* v, ddtree_dtype dt,
+int ddtree_verify_attn(const void* q, const void* k, const void* v, ddtree_dtype dt_arg,
                        const int64_t* kv_offsets, const int32_t* prefix_lens,
                        const int32_t* num_nodes, const uint64_t* mask, int batch, int T, int Hq,
                        int Hkv, int D, int max_prefix_len, int64_t total_rows,
                        float softmax_scale, void* out, int32_t* status_flags, void* workspace,
                        size_t workspace_bytes, void* stream) {
+  const int dt = dtype_value(&dt_arg);
   if (!q || !k || !v || !kv_offsets || !prefix_lens || !num_nodes || !mask || !out)
     return DDTREE_ERR_ARG;
   if (batch < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_prefix_len < 0 || total_rows < 1)
@@ -190,8 +217,9 @@ int ddtree_verify_attn(const void* q, const void* k, const void* v, ddtree_dtype
   if (T > DDTREE_MAX_N + 1) return DDTREE_ERR_UNSUPPORTED;
   if (D != 32 && D != 64 && D != 128) return DDTREE_ERR_UNSUPPORTED;
   if (dt == DDTREE_BF16 && D != 128) return DDTREE_ERR_UNSUPPORTED;
-  if ((long long)batch * T * Hq > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  if (!product_fits_i32(batch, T, Hq)) return DDTREE_ERR_UNSUPPORTED;
   const size_t need = attn_workspace_bytes(dt, batch, T, Hq, Hkv, D, max_prefix_len);
+  if (need == 0) return DDTREE_ERR_UNSUPPORTED;  // the work grid would not fit a launch
   if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
   AttnArgs a{};
   a.q = q;
@@ -216,15 +244,17 @@ int ddtree_verify_attn(const void* q, const void* k, const void* v, ddtree_dtype
 }
 
 size_t ddtree_accept_workspace_size(int batch, int T) {
-  if (batch < 1 || T < 1) return 0;
+  if (batch < 1 || T < 1 || T > DDTREE_MAX_N + 1) return 0;
+  if (!product_fits_i32(batch, T)) return 0;
   return accept_workspace_bytes(batch, T);
 }
 
-int ddtree_accept(const void* target_logits, ddtree_dtype dt, const int32_t* target_ids,
+int ddtree_accept(const void* target_logits, ddtree_dtype dt_arg, const int32_t* target_ids,
                   const int32_t* tokens, const int32_t* parents, const int32_t* num_nodes,
                   int batch, int T, int V, int L, int32_t* accepted, int32_t* accepted_nodes,
                   int32_t* accept_len, int32_t* bonus, int32_t* target_argmax, void* workspace,
                   size_t workspace_bytes, void* stream) {
+  const int dt = dtype_value(&dt_arg);
   if (!tokens || !parents || !num_nodes || !accepted || !accept_len || !bonus)
     return DDTREE_ERR_ARG;
   if (!target_logits && !target_ids) return DDTREE_ERR_ARG;
@@ -232,7 +262,7 @@ int ddtree_accept(const void* target_logits, ddtree_dtype dt, const int32_t* tar
   if (target_logits && V < 1) return DDTREE_ERR_ARG;
   if (target_logits && !dtype_ok(dt)) return DDTREE_ERR_UNSUPPORTED;
   if (T > DDTREE_MAX_N + 1 || L > DDTREE_MAX_L) return DDTREE_ERR_UNSUPPORTED;
-  if ((long long)batch * T > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  if (!product_fits_i32(batch, T)) return DDTREE_ERR_UNSUPPORTED;
   const size_t need = accept_workspace_bytes(batch, T);
   if (!workspace || workspace_bytes < need) return DDTREE_ERR_WORKSPACE;
   AcceptArgs a{};
@@ -255,12 +285,13 @@ int ddtree_accept(const void* target_logits, ddtree_dtype dt, const int32_t* tar
   return hip_status(launch_accept(a, w, static_cast<hipStream_t>(stream)));
 }
 
-int ddtree_accept_sample(const void* target_logits, ddtree_dtype dt, const int32_t* tokens,
+int ddtree_accept_sample(const void* target_logits, ddtree_dtype dt_arg, const int32_t* tokens,
                          const int32_t* parents, const int32_t* num_nodes, int batch, int T, int V,
                          int L, float temperature, uint64_t seed, uint64_t offset,
                          int32_t* accepted, int32_t* accepted_nodes, int32_t* accept_len,
                          int32_t* bonus, int32_t* target_tokens, void* workspace,
                          size_t workspace_bytes, void* stream) {
+  const int dt = dtype_value(&dt_arg);
   if (!target_logits || !tokens || !parents || !num_nodes || !accepted || !accept_len || !bonus)
     return DDTREE_ERR_ARG;
   if (batch < 1 || T < 1 || L < 1 || V < 1) return DDTREE_ERR_ARG;
@@ -269,7 +300,7 @@ int ddtree_accept_sample(const void* target_logits, ddtree_dtype dt, const int32
   if (T > DDTREE_MAX_N + 1 || L > DDTREE_MAX_L) return DDTREE_ERR_UNSUPPORTED;
   // each weight is below 2^45: V <= 2^19 keeps the 64-bit row sum exact
   if (V > DDTREE_MAX_V) return DDTREE_ERR_UNSUPPORTED;
-  if ((long long)batch * T > 0x7FFFFFFFLL) return DDTREE_ERR_UNSUPPORTED;
+  if (!product_fits_i32(batch, T)) return DDTREE_ERR_UNSUPPORTED;
   if (!target_tokens && (!workspace || workspace_bytes < accept_workspace_bytes(batch, T)))
     return DDTREE_ERR_WORKSPACE;
   AcceptArgs a{};
@@ -292,11 +323,12 @@ int ddtree_accept_sample(const void* target_logits, ddtree_dtype dt, const int32
                                          static_cast<hipStream_t>(stream)));
 }
 
-int ddtree_commit_kv(void* k_cache, void* v_cache, ddtree_dtype dt, const int64_t* kv_offsets,
+int ddtree_commit_kv(void* k_cache, void* v_cache, ddtree_dtype dt_arg, const int64_t* kv_offsets,
                      const int32_t* prefix_lens, const int32_t* accept_len,
                      const int32_t* accepted_nodes, const int32_t* bonus, int batch, int Hkv,
                      int D, int L, int T, int64_t total_rows, int32_t* new_prefix_lens,
                      int32_t* next_roots, void* stream) {
+  const int dt = dtype_value(&dt_arg);
   if (!k_cache || !v_cache || !kv_offsets || !prefix_lens || !accept_len || !accepted_nodes ||
       !bonus || !new_prefix_lens)
     return DDTREE_ERR_ARG;

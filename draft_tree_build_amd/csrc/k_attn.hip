@@ -653,9 +653,9 @@ AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int ma
   if (dtype != 0 || D != kD) return s;
   const int g = Hq / Hkv;
   const int R = T * g;
-  s.row_tiles = (R + kTileRows - 1) / kTileRows;
+  s.row_tiles = (int)(((long long)R + kTileRows - 1) / kTileRows);
   const long blocks = (long)batch * Hkv * s.row_tiles;
-  const int tiles = (max_prefix_len + kKeys - 1) / kKeys + (T + kKeys - 1) / kKeys;
+  const int tiles = (int)(((long long)max_prefix_len + kKeys - 1) / kKeys + (T + kKeys - 1) / kKeys);
   const long slots = 2L * device_cus();
   const double t_tile_us = 1.0, t_fixed_us = 3.0, hbm_bytes_per_us = 8.0e6;
   int best = 1;
@@ -673,11 +673,18 @@ AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int ma
     }
   }
   s.nsplit = best;
-  const long nbh = (long)batch * Hkv;
-  s.chunk = nbh >= kXcds ? best : (int)std::max(1L, best * nbh / kXcds);
+  const long long nbh = (long long)batch * Hkv;
+  s.chunk = nbh >= kXcds ? best : (int)std::max(1LL, best * nbh / kXcds);
   s.unit_chunks = (best + s.chunk - 1) / s.chunk;
-  s.units = (int)(nbh * s.unit_chunks);
-  s.per_xcd = (s.units + kXcds - 1) / kXcds * s.chunk * s.row_tiles;
+  const long long units = nbh * s.unit_chunks;
+  const long long per_unit8 = (units + kXcds - 1) / kXcds;
+  // the grid, per_xcd * 8 workgroups, must fit in 31 bits; otherwise no plan
+  if (per_unit8 > 0x7FFFFFFFLL / kXcds / s.chunk / s.row_tiles) {
+    s.nsplit = 0;
+    return s;
+  }
+  s.units = (int)units;
+  s.per_xcd = (int)(per_unit8 * s.chunk * s.row_tiles);
   return s;
 }
 
@@ -697,7 +704,8 @@ hipError_t launch_simple(const AttnArgs& a, hipStream_t st) {
 size_t attn_workspace_bytes(int dtype, int batch, int T, int Hq, int Hkv, int D,
                             int max_prefix_len) {
   const AttnSplit s = plan_split(dtype, batch, T, Hq, Hkv, D, max_prefix_len);
-  if (s.nsplit <= 1) return 256;
+  if (s.nsplit == 0) return 0;  // no launchable grid for this shape
+  if (s.nsplit == 1) return 256;
   const size_t rows = (size_t)s.nsplit * batch * Hkv * s.row_tiles * kTileRows;
   return align_up(rows * kD * 4, 256) + align_up(rows * 2 * 4, 256);
 }
@@ -712,6 +720,7 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   // f32 (any D); bf16 is D = 128 only (checked by the caller)
   if (a.dtype == 1) return launch_simple(a, st);
   const AttnSplit s = plan_split(a.dtype, a.batch, a.T, a.Hq, a.Hkv, a.D, a.max_prefix_len);
+  if (s.nsplit == 0) return hipErrorInvalidConfiguration;
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (s.nsplit > 1) {

@@ -46,6 +46,15 @@ enum {
                                     scratch than DDTREE_BUILD_SCRATCH_MAX    */
 };
 
+/*
+ * Conventions. Every call checks its arguments on the host before it
+ * enqueues anything; a rejected call returns its status and has no effect.
+ * A dtype argument outside the enumerators (callers may pass any int) gives
+ * DDTREE_ERR_UNSUPPORTED. The *_workspace_size queries return 0 for a shape
+ * outside the limits of their call; products of sizes (batch * L,
+ * batch * T, batch * T * Hq) must fit in 31 bits.
+ */
+
 /* Limits. */
 #define DDTREE_MAX_L 64        /* draft block length (positions)           */
 #define DDTREE_MAX_K 32        /* candidates per position                  */

@@ -414,8 +414,9 @@ void oracle_attn_rows(const void *q, const void *k, const void *v, int dtype,
             o[d] = 0.0;
         if (i >= num_nodes[b])
             continue;
+        /* written so that no sum can overflow */
         if (kv_offsets[b] < 0 || prefix_lens[b] < 0 ||
-            kv_offsets[b] + prefix_lens[b] + T > total_rows)
+            kv_offsets[b] > total_rows - (int64_t)prefix_lens[b] - T)
             continue;
         int P = prefix_lens[b];
         int hk = h / g;
@@ -686,7 +687,7 @@ void oracle_commit_kv(void *k_cache, void *v_cache, size_t row_bytes, const int6
         const int64_t off = kv_offsets[b];
         const int64_t P = prefix_lens[b];
         const int32_t *a = accepted_nodes + (size_t)b * L;
-        int ok = n >= 0 && n <= L && n <= T - 1 && off >= 0 && P >= 0 && off + P + T <= total_rows;
+        int ok = n >= 0 && n <= L && n <= T - 1 && off >= 0 && P >= 0 && off <= total_rows - P - T;
         for (int k = 0; ok && k < n; ++k)
             if (a[k] < 1 || a[k] >= T)
                 ok = 0;
