@@ -15,10 +15,11 @@
 // registers), row-major with an XOR swizzle of the 16-byte chunks; V
 // fragments come out transposed through ds_read_b64_tr_b16. Per wave and
 // tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
-// (lane = query row), online softmax in fp32 (exp2 domain), O^T += V^T P^T
-// on v_mfma_f32_32x32x16_f16: each V tile is converted to fp16 in LDS once
-// (every wave converts the rows it staged), and P enters as fp16 (2^-12
-// relative per weight, against 2^-9 for bf16 weights).
+// (lane = query row), online softmax in fp32 (exp2 domain) against a
+// running reference that moves only when the weights would leave the fp16
+// range, O^T += V^T P^T on v_mfma_f32_32x32x16_f16: each V tile is converted
+// to fp16 in LDS once (every wave converts the rows it staged), and P enters
+// as fp16 (2^-12 relative per weight, against 2^-9 for bf16 weights).
 // The key tile list is prefix tiles then tree tiles (mask applied); long
 // lists are split across workgroups and merged by a second kernel
 // (log-sum-exp weights).
@@ -60,18 +61,21 @@ __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 +
 // fp16 subnormals (absolute error <= 2^-25). Called after the wave's own
 // DMA has landed and before the barrier that publishes the tile.
 __device__ __forceinline__ void v_tile_to_f16(unsigned char* vbuf, int w, int lane) {
+  // all four reads first: one LDS round trip instead of four
+  uint4 u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) u[j] = *reinterpret_cast<const uint4*>(vbuf + (4 * w + j) * 1024 + 16 * lane);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint4* p = reinterpret_cast<uint4*>(vbuf + (4 * w + j) * 1024 + 16 * lane);
-    const uint4 u = *p;
-    const uint32_t in[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t in[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
     uint32_t o[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const floatx2 f = {__uint_as_float(in[q] << 16), __uint_as_float(in[q] & 0xFFFF0000u)};
       o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, halfx2));
     }
-    *p = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(vbuf + (4 * w + j) * 1024 + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -204,7 +208,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  // padding rows (no keys, zero Q) take a finite reference from the start
+  float m_run = row_valid ? -INFINITY : 0.0f, l_run = 0.0f;
 
   // ---- staging by DMA: wave w moves rows 16 w .. 16 w + 15 of K and V, four
   // 1 KB blocks each; lane i of a block writes LDS bytes 16 i of it, so it
@@ -280,12 +285,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   auto load_mword = [&](int t) __attribute__((always_inline)) -> uint64_t {
     return (t >= np && row_valid) ? mrow[t - np] : 0ull;
   };
-  // One key tile from LDS (kl, vl: the tile's K and V buffers). Both 32-key
-  // halves of S^T are computed first (two independent MFMA chains), the
-  // online softmax then covers the whole tile (one maximum update), and the
-  // exponentials of the second half run on the VALU while the first half's
-  // O^T += V^T P^T products occupy the matrix core.
-  auto tile_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl)
+  // One key tile from LDS (kl, vl: the tile's K and V buffers; nk, nv: the
+  // other buffers, where the next tile's DMA goes when has_next). Both
+  // 32-key halves of S^T are computed first (two independent MFMA chains);
+  // the weights of each half are then taken against the row's running
+  // reference, and the exponentials of the second half run on the VALU
+  // while the first half's O^T += V^T P^T products occupy the matrix core.
+  uint64_t mword_next = 0;
+  auto tile_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl,
+                       unsigned char* nk, unsigned char* nv, bool has_next)
       __attribute__((always_inline)) {
     int base, nvalid;
     tile_rows(t, &base, &nvalid);
@@ -301,13 +309,29 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sc[kb][v] = 0.0f;
+    // K fragments read two steps ahead of their MFMAs (four in flight)
+    bf16x8 kf[8][2];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + kb * 32 * 256);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 2; ++kb)
+        kf[ks][kb] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + kb * 32 * 256);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kb], qf[ks], sc[kb], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // the next tile's DMA is issued while the score MFMAs run
+    if (has_next) {
+      dma_tile(t + 1, nk, nv);
+      mword_next = load_mword(t + 1);
     }
     // V fragments of the first half, read while the scores are computed
     auto read_v = [&](int kb, halfx8 (&vf)[4][2]) __attribute__((always_inline)) {
@@ -324,59 +348,62 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     halfx8 vf[4][2];
     read_v(0, vf);
 
-    // ---- mask (tree tiles and the ragged last prefix tile only) and row max.
-    // Query rows past num_nodes need no masking: their scores never reach a
-    // valid row and their outputs are written as zeros.
-    float tmax = -INFINITY;
+    // ---- mask (tree tiles and the ragged last prefix tile only). Query rows
+    // past num_nodes need no masking: their scores never reach a valid row
+    // and their outputs are written as zeros.
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (need_mask) {
+      for (int kb = 0; kb < 2; ++kb) {
         // register v holds key 32 kb + 8 gq + v (v < 8) or + 8 more (v >= 8)
         const uint32_t sh = 32 * kb + 8 * gq;
         const uint32_t bits = (uint32_t)((allow >> sh) & 0xFFull) | ((uint32_t)((allow >> (sh + 16)) & 0xFFull) << 8);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          sc[kb][v] = ((bits >> v) & 1u) ? sc[kb][v] : -INFINITY;
-          tmax = fmaxf(tmax, sc[kb][v]);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sc[kb][v]);
+        for (int v = 0; v < 16; ++v) sc[kb][v] = ((bits >> v) & 1u) ? sc[kb][v] : -INFINITY;
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // The reference m_run of the exponentials moves only when a row's
-    // maximum passes it by more than 8 (log2 units): weights then stay below
-    // 2^8, and O and l are rescaled on few tiles (O and l share the
-    // reference, so the final O / l is unchanged).
-    const float m_new = fmaxf(m_run, tmax * c_log2);
-    float alpha = 1.0f;
-    if (__ballot(m_new > m_run + 8.0f) != 0) {
-      alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.0f : m_new));
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-    // P enters the MFMA as fp16: weights are below 2^8, so fp16 keeps
-    // 2^-12 of each (subnormal below 2^-14, absolute error <= 2^-25).
-    float psum = 0.0f;
-    auto probs = [&](int kb, halfx8 (&pf)[2]) __attribute__((always_inline)) {
+    // Weights p = 2^(s c - m_run) against the row's reference m_run, taken
+    // without a maximum. The reference is an exact running maximum of the
+    // row's scores, re-taken only where it has to move: on a half tile whose
+    // weights sum to more than 2^15 (or to no finite value), and while a row
+    // has met no key (m_run = -inf). Weights then stay below 2^15, inside
+    // fp16; O and l share the reference, so O / l is unchanged. The row sum
+    // l adds the fp16 weights that enter the P.V product (v_dot2_f32_f16
+    // with fp32 accumulation).
+    auto probs = [&](int kb, halfx8 (&pf)[2]) __attribute__((always_inline)) -> float {
+      const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
+      float ps = 0.0f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         halfx2 h2[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           floatx2 pr;
-          pr[0] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2], c_log2, -m_use));
-          pr[1] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2 + 1], c_log2, -m_use));
-          psum += pr[0] + pr[1];
+          pr[0] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2], c_log2, neg_m));
+          pr[1] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2 + 1], c_log2, neg_m));
           h2[e2] = __builtin_convertvector(pr, halfx2);
+          ps = __builtin_amdgcn_fdot2(h2[e2], halfx2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
         }
         pf[hf] = halfx8{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
       }
+      return ps;
+    };
+    // the rare path: the half tile's exact maximum becomes the reference
+    // where it is larger, O and l are rescaled, the weights recomputed
+    auto settle = [&](int kb, halfx8 (&pf)[2], float& ps) __attribute__((always_inline)) {
+      if (__ballot(m_run == -INFINITY || !(ps <= 32768.0f)) == 0ull) return;
+      float hmax = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hmax = fmaxf(hmax, sc[kb][v]);
+      hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+      const float m_new = fmaxf(m_run, hmax * c_log2);
+      const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      ps = probs(kb, pf);
     };
     auto pv = [&](const halfx8 (&vfr)[4][2], const halfx8 (&pf)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -386,19 +413,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
           acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
     };
     halfx8 pf0[2];
-    probs(0, pf0);
+    float ps0 = probs(0, pf0);
+    settle(0, pf0, ps0);
     pv(vf, pf0);
+    l_run += ps0;
+    halfx8 vf1[4][2];
+    read_v(1, vf1);
     halfx8 pf1[2];
-    probs(1, pf1);
-    read_v(1, vf);
-    pv(vf, pf1);
-    l_run = l_run * alpha + psum;
+    float ps1 = probs(1, pf1);
+    settle(1, pf1, ps1);
+    pv(vf1, pf1);
+    l_run += ps1;
   };
 
   // Tiles alternate between two LDS buffers (static, so that the compiler
   // sees the DMA into one buffer and the reads of the other as disjoint):
   // while tile t is computed from one buffer, tile t+1 lands in the other.
-  uint64_t mword_next = 0;
   if (t_begin < t_end) {
     dma_tile(t_begin, k_lds0, v_lds0);
     mword_next = load_mword(t_begin);
@@ -409,22 +439,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   for (int t = t_begin; t < t_end; t += 2) {
     {
       const uint64_t mword = mword_next;
-      if (t + 1 < t_end) {
-        dma_tile(t + 1, k_lds1, v_lds1);
-        mword_next = load_mword(t + 1);
-      }
-      tile_body(t, mword, k_lds0, v_lds0);
+      tile_body(t, mword, k_lds0, v_lds0, k_lds1, v_lds1, t + 1 < t_end);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
       if (t + 1 < t_end) v_tile_to_f16(v_lds1, w, lane);
       __syncthreads();
     }
     if (t + 1 < t_end) {
       const uint64_t mword = mword_next;
-      if (t + 2 < t_end) {
-        dma_tile(t + 2, k_lds0, v_lds0);
-        mword_next = load_mword(t + 2);
-      }
-      tile_body(t + 1, mword, k_lds1, v_lds1);
+      tile_body(t + 1, mword, k_lds1, v_lds1, k_lds0, v_lds0, t + 2 < t_end);
       __builtin_amdgcn_s_waitcnt(0);
       if (t + 2 < t_end) v_tile_to_f16(v_lds0, w, lane);
       __syncthreads();

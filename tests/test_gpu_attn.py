@@ -149,6 +149,33 @@ def test_attn_bf16_batch_beyond_xcds_all_rows():
     assert np.all(st == 0), st
 
 
+def test_attn_bf16_reference_moves_all_rows():
+    """Scores that rise along the prefix (K rows scaled up to 6x, so the
+    exponentials' running reference has to move on many key tiles), one key
+    near the end of a prefix far above all others (a late jump of ~50 in
+    log2 units), a tree-only request and a split-KV request: every row."""
+    B, L, V, K, N, Hq, Hkv, P = 3, 6, 60, 6, 64, 32, 8, [2000, 1300, 0]
+    T = N + 1
+    tree = _tree(B, L, V, K, N, seed=77)
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=77)
+    kf = k.float()
+    offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
+    for b in range(2):
+        o = int(offs[b])
+        ramp = 1.0 + 5.0 * torch.arange(P[b], dtype=torch.float32) / P[b]
+        kf[o:o + P[b]] *= ramp[:, None, None]
+    g = Hq // Hkv
+    qm = q.float()[1].reshape(T, Hkv, g, 128).mean(dim=(0, 2))      # [Hkv, D]
+    kf[int(offs[1]) + P[1] - 3] = 3.0 * qm / qm.norm(dim=1, keepdim=True) * 11.0
+    kf[int(offs[1]) + P[1] - 5, 0] = 3.0 * q.float()[1, 5, 0]    # row 5, head 0: +~49 (log2)
+    k = kf.to(torch.bfloat16)
+    note("attn bf16 reference moves P=%s" % P)
+    out, offs2, st = _run(q, k, v, P, tree, T, offs=offs)
+    sel = _all_rows(B, T, Hq)
+    check_attn(out, _ref(q, k, v, offs2, P, tree, T, sel), sel, torch.bfloat16)
+    assert np.all(st == 0), st
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 def test_attn_f32_all_rows(D):
     B, L, V, K, N, Hq, Hkv, P = 2, 4, 30, 4, 8, 4, 2, [16, 3]
