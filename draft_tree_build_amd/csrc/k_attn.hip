@@ -99,7 +99,50 @@ struct AttnSplit {
   int unit_chunks;  // units per (request, kv-head): ceil(nsplit / chunk)
   int units;        // batch * Hkv * unit_chunks
   int per_xcd;      // workgroups per XCD: ceil(units / 8) * chunk * row_tiles
+  int preconv;      // V converted to fp16 once per request before the main kernel
 };
+
+// V is converted to fp16 by a separate pass (k_v_f16) when this many row
+// tiles or more read every K/V tile: each of them would otherwise convert
+// its V tiles again (measured: the in-kernel conversion costs 8.6% of the
+// verify at 33 row tiles; the pass moves the request's V bytes twice).
+constexpr int kPreconvMinRowTiles = 16;
+constexpr size_t kPreconvMaxBytes = (size_t)4 << 30;
+
+// fp16 copy of the V rows the verify reads: request b's rows [0, P_b + T)
+// at vh + (b * (max_prefix_len + T) + row) * Hkv * 128, the same rounding as
+// v_tile_to_f16. Requests outside the caches or with P_b > max_prefix_len
+// are skipped (the main kernel converts those itself). Grid: x = chunks of
+// 2048 16-byte vectors, y = request.
+__global__ __launch_bounds__(256) void k_v_f16(AttnArgs a, uint16_t* vh) {
+  const int b = (int)blockIdx.y;
+  const int64_t kv0 = a.kv_offsets[b];
+  const int P = a.prefix_lens[b];
+  if (!kv_in_range(kv0, P, a.T, a.total_rows) || P > a.max_prefix_len) return;
+  const int64_t vecs = ((int64_t)P + a.T) * a.Hkv * (kD / 8);
+  const int64_t base = (int64_t)blockIdx.x * 2048;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + kv0 * a.Hkv * kD);
+  uint4* dst = reinterpret_cast<uint4*>(vh + (size_t)b * (a.max_prefix_len + a.T) * a.Hkv * kD);
+  uint4 u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t i = base + j * 256 + threadIdx.x;
+    u[j] = i < vecs ? src[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t i = base + j * 256 + threadIdx.x;
+    if (i >= vecs) break;
+    const uint32_t in[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const floatx2 f = {__uint_as_float(in[q] << 16), __uint_as_float(in[q] & 0xFFFF0000u)};
+      o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, halfx2));
+    }
+    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
 
 constexpr int kXcds = 8;
 
@@ -115,7 +158,7 @@ constexpr int kXcds = 8;
 // tiles are double-buffered in LDS: tile t+1 is fetched into registers while
 // tile t is computed.
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, float* part_o,
-                                                      float* part_ml) {
+                                                      float* part_ml, const uint16_t* vh) {
   // two buffers of K and V tiles; 64 KB
   __shared__ __attribute__((aligned(16))) unsigned char k_lds0[kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds0[kTileBytes];
@@ -189,6 +232,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   const int per = (ntiles + nsplit - 1) / nsplit;
   const int t_begin = min(z * per, ntiles), t_end = min(t_begin + per, ntiles);
   const size_t kv0 = (size_t)kv0s;
+  // V tiles come converted to fp16 from k_v_f16 when it ran for this request
+  const bool pre = vh != nullptr && P <= a.max_prefix_len;
+  const size_t vrow0 = (size_t)b * ((size_t)a.max_prefix_len + T);
   const int W = (T + 63) >> 6;
   const float c_log2 = a.scale * kLog2e;
 
@@ -242,7 +288,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     // tile holds at least one valid key
     const size_t tb = (kv0 + (size_t)base) * row_bytes;
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(Kg) + tb;
-    const unsigned char* vt = reinterpret_cast<const unsigned char*>(Vg) + tb;
+    const unsigned char* vt =
+        pre ? reinterpret_cast<const unsigned char*>(vh) + (vrow0 + (size_t)base) * row_bytes
+            : reinterpret_cast<const unsigned char*>(Vg) + tb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // rows past the tile's nvalid keys re-read the tile's first row: their
@@ -434,21 +482,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     mword_next = load_mword(t_begin);
   }
   __builtin_amdgcn_s_waitcnt(0);
-  if (t_begin < t_end) v_tile_to_f16(v_lds0, w, lane);
+  if (t_begin < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
   __syncthreads();
   for (int t = t_begin; t < t_end; t += 2) {
     {
       const uint64_t mword = mword_next;
       tile_body(t, mword, k_lds0, v_lds0, k_lds1, v_lds1, t + 1 < t_end);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
-      if (t + 1 < t_end) v_tile_to_f16(v_lds1, w, lane);
+      if (t + 1 < t_end && !pre) v_tile_to_f16(v_lds1, w, lane);
       __syncthreads();
     }
     if (t + 1 < t_end) {
       const uint64_t mword = mword_next;
       tile_body(t + 1, mword, k_lds1, v_lds1, k_lds0, v_lds0, t + 2 < t_end);
       __builtin_amdgcn_s_waitcnt(0);
-      if (t + 2 < t_end) v_tile_to_f16(v_lds0, w, lane);
+      if (t + 2 < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
       __syncthreads();
     }
   }
@@ -666,12 +714,17 @@ int device_cus() {
   return cus[dev];
 }
 
+// Bytes of the fp16 V copy: max_prefix_len + T rows per request.
+size_t vh_bytes(int batch, int T, int Hkv, int max_prefix_len) {
+  return (size_t)batch * ((size_t)max_prefix_len + T) * Hkv * kD * 2;
+}
+
 // Split of each row tile's key range across workgroups: pick the count that
 // minimises a simple time model -- rounds of resident workgroups (two per
 // CU) times the key tiles per workgroup, plus the partial-result traffic of
 // the merge -- with at least 4 key tiles per split.
 AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int max_prefix_len) {
-  AttnSplit s{1, 0, 1, 1, 0, 0};
+  AttnSplit s{1, 0, 1, 1, 0, 0, 0};
   if (dtype != 0 || D != kD) return s;
   const int g = Hq / Hkv;
   const int R = T * g;
@@ -707,6 +760,10 @@ AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int ma
   }
   s.units = (int)units;
   s.per_xcd = (int)(per_unit8 * s.chunk * s.row_tiles);
+  s.preconv = (s.row_tiles >= kPreconvMinRowTiles && batch <= 65535 &&
+               vh_bytes(batch, T, Hkv, max_prefix_len) <= kPreconvMaxBytes)
+                  ? 1
+                  : 0;
   return s;
 }
 
@@ -727,9 +784,13 @@ size_t attn_workspace_bytes(int dtype, int batch, int T, int Hq, int Hkv, int D,
                             int max_prefix_len) {
   const AttnSplit s = plan_split(dtype, batch, T, Hq, Hkv, D, max_prefix_len);
   if (s.nsplit == 0) return 0;  // no launchable grid for this shape
-  if (s.nsplit == 1) return 256;
-  const size_t rows = (size_t)s.nsplit * batch * Hkv * s.row_tiles * kTileRows;
-  return align_up(rows * kD * 4, 256) + align_up(rows * 2 * 4, 256);
+  size_t bytes = 0;
+  if (s.nsplit > 1) {
+    const size_t rows = (size_t)s.nsplit * batch * Hkv * s.row_tiles * kTileRows;
+    bytes = align_up(rows * kD * 4, 256) + align_up(rows * 2 * 4, 256);
+  }
+  if (s.preconv) bytes += align_up(vh_bytes(batch, T, Hkv, max_prefix_len), 256);
+  return bytes ? bytes : 256;
 }
 
 hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
@@ -745,15 +806,25 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   if (s.nsplit == 0) return hipErrorInvalidConfiguration;
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  char* p = static_cast<char*>(ws);
   if (s.nsplit > 1) {
     const size_t rows = (size_t)s.nsplit * a.batch * a.Hkv * s.row_tiles * kTileRows;
-    char* p = static_cast<char*>(ws);
     part_o = reinterpret_cast<float*>(p);
     p += align_up(rows * kD * 4, 256);
     part_ml = reinterpret_cast<float*>(p);
+    p += align_up(rows * 2 * 4, 256);
+  }
+  uint16_t* vh = nullptr;
+  if (s.preconv) {
+    vh = reinterpret_cast<uint16_t*>(p);
+    const int64_t vecs = ((int64_t)a.max_prefix_len + a.T) * a.Hkv * (kD / 8);
+    hipLaunchKernelGGL(k_v_f16, dim3((unsigned)((vecs + 2047) / 2048), a.batch), dim3(256), 0, st,
+                       a, vh);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   dim3 grid(s.per_xcd * kXcds), block(256);
-  hipLaunchKernelGGL(k_attn_mfma, grid, block, 0, st, a, s, part_o, part_ml);
+  hipLaunchKernelGGL(k_attn_mfma, grid, block, 0, st, a, s, part_o, part_ml, (const uint16_t*)vh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s.nsplit <= 1) return e;
   const int R = a.T * (a.Hq / a.Hkv);

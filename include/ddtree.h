@@ -178,7 +178,12 @@ int ddtree_mask(const int32_t *parents, const int32_t *num_nodes, int batch, int
  *   softmax_scale <= 0 selects 1/sqrt(D)
  *   status_flags  [batch] int32 or NULL                 out: DDTREE_STATUS_OUT_NONFINITE,
  *                 DDTREE_STATUS_BAD_KV (0 when neither holds)
- *   workspace     >= ddtree_verify_workspace_size(...) bytes
+ *   workspace     >= ddtree_verify_workspace_size(...) bytes: the split-key
+ *                 partials, and (bf16, when 16 or more 128-row tiles per
+ *                 (request, kv-head) would each convert the same V tiles)
+ *                 an fp16 copy of the V rows read, batch * (max_prefix_len
+ *                 + T) rows; a request with P_b > max_prefix_len converts
+ *                 its own tiles instead (same values)
  *
  * Request b's rows are checked on the device (the offsets and lengths may
  * come from earlier kernels): kv_offsets[b] >= 0, P_b >= 0 and

@@ -176,6 +176,36 @@ def test_attn_bf16_reference_moves_all_rows():
     assert np.all(st == 0), st
 
 
+def test_attn_bf16_preconverted_v():
+    """33 row tiles per (request, kv-head) (T = 513, g = 8): V goes to fp16
+    in a pass of its own before the main kernel. A request whose prefix
+    exceeds max_prefix_len converts its own tiles; a request whose K/V rows
+    end past the caches gets zero rows and the BAD_KV bit. Every row of one
+    query head per kv-head, and each request's last rows of every head."""
+    B, L, V, K, N, Hq, Hkv = 3, 6, 60, 6, 512, 64, 8
+    T = N + 1
+    P = [1500, 700, 2100]
+    max_prefix = 1600                     # request 2 is longer
+    tree = _tree(B, L, V, K, N, seed=513)
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=513)
+    ws_pre = api.ddtree_verify_workspace_size(0, B, T, Hq, Hkv, 128, max_prefix)
+    assert ws_pre >= B * (max_prefix + T) * Hkv * 128 * 2      # the fp16 copy is planned
+    offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
+    total = k.shape[0]
+    offs_bad = offs.clone()
+    offs_bad[1] = total - P[1] - T + 1    # one row past the end
+    note("attn bf16 preconverted V P=%s max_prefix=%d" % (P, max_prefix))
+    out, offs2, st = _run(q, k, v, P, tree, T, max_prefix=max_prefix, offs=offs_bad)
+    g = Hq // Hkv
+    heads = [hk * g + (hk * 3) % g for hk in range(Hkv)]
+    sel = [(b, i, h) for b in range(B) for i in range(T) for h in heads]
+    sel += [(b, i, h) for b in range(B) for i in range(T - 3, T) for h in range(Hq)]
+    sel = sorted(set(sel))
+    check_attn(out, _ref(q, k, v, offs2, P, tree, T, sel), sel, torch.bfloat16)
+    assert torch.all(out[1] == 0)
+    assert st.tolist() == [0, 8, 0], st
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 def test_attn_f32_all_rows(D):
     B, L, V, K, N, Hq, Hkv, P = 2, 4, 30, 4, 8, 4, 2, [16, 3]
