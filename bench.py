@@ -57,7 +57,8 @@ KERNEL_SOURCES = {
     "commit": ["draft_tree_build_amd/csrc/k_commit.hip"],
 }
 KERNEL_NAMES = {"build": "ddtree_build: k_rows (+ k_rows_sum for split rows), k_tree",
-                "verify": "ddtree_verify_attn: k_attn_mfma (+ k_attn_combine for split keys)",
+                "verify": "ddtree_verify_attn: k_attn_mfma (+ k_v_f16 before it when many row tiles "
+                          "share each V tile, + k_attn_combine for split keys)",
                 "accept": "ddtree_accept: k_argmax, k_walk",
                 "accept_sample": "ddtree_accept_sample: k_sample, k_walk",
                 "commit": "ddtree_commit_kv: k_commit"}
@@ -442,7 +443,7 @@ def summarize_traffic(fetch_csv, write_csv, workload, commands):
     copy_kib = 256 * 1024
     ff, wf = copy_kib / cf, copy_kib / cw
     stages = {"build": ["k_rows", "k_rows_sum", "k_tree", "k_tree_level"],
-              "verify": ["k_attn_mfma", "k_attn_combine", "k_attn_simple"],
+              "verify": ["k_v_f16", "k_attn_mfma", "k_attn_combine", "k_attn_simple"],
               "accept": ["k_argmax", "k_walk"], "accept_sample": ["k_sample"],
               "commit": ["k_commit"]}
     res = {}
