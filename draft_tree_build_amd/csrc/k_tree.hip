@@ -1015,13 +1015,19 @@ __global__ __launch_bounds__(kLB) void k_tree_level(TreeArgs a) {
 
 // Both kernels build the same tree. The pops of k_tree cost ~0.2-0.3 us
 // each; k_tree_level costs a roughly fixed number of workgroup-wide steps
-// (~25-45 us per request whatever N). Measured crossover: the pops win up
-// to N = 128 (17.8 against ~27 us at N = 64), the level selection from
-// N = 256 (31 against 73 us at N = 256, 46 against 165 us at N = 512).
-constexpr int kLevelMinN = 129;
+// (~25-45 us per request whatever N). Measured (build stage, V = 32,000 and
+// 151,936, L = 16): the pops win up to N = 80, the level selection from
+// N = 96 (44 against 51 and 46 against 56 us at N = 128; 46 against 165 us
+// at N = 512); at 32 requests the two tie at N = 128. In argmax mode
+// (draft temperature 0) almost every prefix ties at score -inf, which the
+// level selection places in a slower final phase (~87 us against ~50 us for
+// the pops at N = 128), so there the pops are kept up to N = 383.
+constexpr int kLevelMinN = 97;
+constexpr int kLevelMinNArgmax = 384;
 
 hipError_t launch_tree(const TreeArgs& t, int batch, hipStream_t st) {
-  if (t.N >= kLevelMinN) hipLaunchKernelGGL(k_tree_level, dim3(batch), dim3(kLB), 0, st, t);
+  const int min_n = t.mode == 2 ? kLevelMinNArgmax : kLevelMinN;
+  if (t.N >= min_n) hipLaunchKernelGGL(k_tree_level, dim3(batch), dim3(kLB), 0, st, t);
   else hipLaunchKernelGGL(k_tree, dim3(batch), dim3(kBlock), 0, st, t);
   return hipGetLastError();
 }
