@@ -248,13 +248,16 @@ def _few_values(B, L, V, seed, values):
     (6, 400, 12, 500, "few"), (16, 600, 16, 1024, "few"), (3, 50, 32, 1024, "few"),
     (64, 300, 2, 1000, "few"), (4, 40, 4, 1024, "normal"),   # budget above the restricted set (340)
     (40, 300, 1, 200, "normal"), (12, 700, 8, 257, "peaked"),
+    (8, 500, 8, 96, "few"), (8, 500, 8, 97, "few"),   # the two sides of the kernel switch
 ])
 @pytest.mark.parametrize("tau", [1.0, 0.7, 0.0])
 def test_build_level_selection(L, V, K, N, kind, tau):
-    """Budgets above 128 run the level-synchronous selection: ties at the
-    threshold score (bf16 logits from a handful of values, temperature 0's
-    -inf tails), budgets above the restricted set (padding rows), K = 1
-    chains, deep trees under a peaked drafter."""
+    """Budgets from 97 (from 384 at temperature 0) run the level-synchronous
+    selection, smaller ones the heap's pops; both must give the oracle's
+    heap tree: ties at the threshold score (bf16 logits from a handful of
+    values, temperature 0's -inf tails), budgets above the restricted set
+    (padding rows), K = 1 chains, deep trees under a peaked drafter, and the
+    two budgets on either side of the switch."""
     B = 2
     if kind == "few":
         x = _few_values(B, L, V, seed=L * V + N, values=[2.0, 1.0, 1.0, 0.5, 0.0, -1.0])
