@@ -1019,11 +1019,12 @@ __global__ __launch_bounds__(kLB) void k_tree_level(TreeArgs a) {
 // 151,936, L = 16): the pops win up to N = 80, the level selection from
 // N = 96 (44 against 51 and 46 against 56 us at N = 128; 46 against 165 us
 // at N = 512); at 32 requests the two tie at N = 128. In argmax mode
-// (draft temperature 0) almost every prefix ties at score -inf, which the
-// level selection places in a slower final phase (~87 us against ~50 us for
-// the pops at N = 128), so there the pops are kept up to N = 383.
+// (draft temperature 0) the level selection walks every depth with a few
+// parents each, at a near-fixed ~87 us, while the pops cost ~0.3 us each:
+// 69 against 88 us at N = 160, 89 against 87 us at N = 224, 99 against 88 us
+// at N = 256 (V = 151,936, K = 16), so there the pops run up to N = 223.
 constexpr int kLevelMinN = 97;
-constexpr int kLevelMinNArgmax = 384;
+constexpr int kLevelMinNArgmax = 224;
 
 hipError_t launch_tree(const TreeArgs& t, int batch, hipStream_t st) {
   const int min_n = t.mode == 2 ? kLevelMinNArgmax : kLevelMinN;
