@@ -721,7 +721,34 @@ __global__ __launch_bounds__(kLB) void k_tree_level(TreeArgs a) {
     // runs (binary searches in the sorted row), their offsets (a scan), and
     // the children written on a (parent, rank) grid, one child per thread.
     bool full = false;
-    {
+    if (nparents <= 64) {
+      // Few parents: wave 0 alone counts their runs, scans them by DPP and
+      // writes the children (a lane per parent, its run in rank order), and
+      // one barrier publishes them; the same positions as the grid below.
+      if (tid < 64) {
+        const float ps = d == 1 ? 0.0f : (tid < nparents ? sh.s_score[prev_b + tid] : 0.0f);
+        const int c = tid < nparents ? count_ranks<true>(ps, lrow, K, th) : 0;
+        const int incl = wave_scan_dpp(c);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (total <= kCap - nS) {
+          const int q0 = nS + incl - c;
+          for (int r = 0; r < c; ++r) {
+            sh.s_score[q0 + r] = ps + lrow[r];
+            sh.s_par[q0 + r] = d == 1 ? kRootRef : (uint16_t)(prev_b + tid);
+            sh.s_depth[q0 + r] = (uint8_t)d;
+            sh.s_rank[q0 + r] = (uint8_t)r;
+          }
+        }
+        if (tid == 0) sh.bc[3] = total;
+      }
+      __syncthreads();
+      const int total = sh.bc[3];
+      if (total <= kCap - nS) {
+        nS += total;
+        cur = nparents;
+        full = nS >= N;
+      }
+    } else {
       for (int j = tid; j < nparents; j += kLB)
         sh.s_tmp[j] = count_ranks<true>(d == 1 ? 0.0f : sh.s_score[prev_b + j], lrow, K, th);
       __syncthreads();
@@ -1015,16 +1042,16 @@ __global__ __launch_bounds__(kLB) void k_tree_level(TreeArgs a) {
 
 // Both kernels build the same tree. The pops of k_tree cost ~0.2-0.3 us
 // each; k_tree_level costs a roughly fixed number of workgroup-wide steps
-// (~25-45 us per request whatever N). Measured (build stage, V = 32,000 and
-// 151,936, L = 16): the pops win up to N = 80, the level selection from
-// N = 96 (44 against 51 and 46 against 56 us at N = 128; 46 against 165 us
-// at N = 512); at 32 requests the two tie at N = 128. In argmax mode
-// (draft temperature 0) the level selection walks every depth with a few
-// parents each, at a near-fixed ~87 us, while the pops cost ~0.3 us each:
-// 69 against 88 us at N = 160, 89 against 87 us at N = 224, 99 against 88 us
-// at N = 256 (V = 151,936, K = 16), so there the pops run up to N = 223.
-constexpr int kLevelMinN = 97;
-constexpr int kLevelMinNArgmax = 224;
+// (~25-45 us per request whatever N). Measured (build stage, L = 16,
+// V = 32,000 / 151,936): the pops win at N = 64 (35.4 / 43.6 against
+// 35.9 / 45.4 us), the level selection from N = 80 (39.7 / 45.6 against
+// 41.5 / 49.0 us; 46 against 165 us at N = 512). In argmax mode (draft
+// temperature 0) the level selection walks every depth with a few parents
+// each, at a near-fixed ~69 us, while the pops cost ~0.3 us each: 58
+// against 69 us at N = 128, equal at N = 160, 79 against 70 us at N = 192
+// (V = 151,936, K = 16).
+constexpr int kLevelMinN = 72;
+constexpr int kLevelMinNArgmax = 160;
 
 hipError_t launch_tree(const TreeArgs& t, int batch, hipStream_t st) {
   const int min_n = t.mode == 2 ? kLevelMinNArgmax : kLevelMinN;

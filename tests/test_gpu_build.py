@@ -248,12 +248,13 @@ def _few_values(B, L, V, seed, values):
     (6, 400, 12, 500, "few"), (16, 600, 16, 1024, "few"), (3, 50, 32, 1024, "few"),
     (64, 300, 2, 1000, "few"), (4, 40, 4, 1024, "normal"),   # budget above the restricted set (340)
     (40, 300, 1, 200, "normal"), (12, 700, 8, 257, "peaked"),
-    (8, 500, 8, 96, "few"), (8, 500, 8, 97, "few"),   # the two sides of the kernel switch
-    (10, 400, 16, 223, "few"), (10, 400, 16, 224, "few"),   # same at temperature 0
+    (8, 500, 8, 71, "few"), (8, 500, 8, 72, "few"),   # the two sides of the kernel switch
+    (10, 400, 16, 159, "few"), (10, 400, 16, 160, "few"),   # same at temperature 0
+    (16, 600, 8, 100, "normal"), (20, 900, 16, 140, "peaked")
 ])
 @pytest.mark.parametrize("tau", [1.0, 0.7, 0.0])
 def test_build_level_selection(L, V, K, N, kind, tau):
-    """Budgets from 97 (from 224 at temperature 0) run the level-synchronous
+    """Budgets from 72 (from 160 at temperature 0) run the level-synchronous
     selection, smaller ones the heap's pops; both must give the oracle's
     heap tree: ties at the threshold score (bf16 logits from a handful of
     values, temperature 0's -inf tails), budgets above the restricted set
