@@ -10,12 +10,16 @@ trees with padding rows, GQA group sizes 1/4/8, row tiles with a ragged tail,
 the split-KV path with requests of different lengths and with fewer
 (request, kv-head) pairs than XCDs); the largest tree (T = 1025, split keys,
 ragged prefixes and a ragged last row tile) and a batch of more requests than
-XCDs compare every row as well. The full-size workloads run in the launch
-configuration the benchmark times and compare at least one row of every
-(request, kv-head, 128-row tile) unit of the kernel, every row of one query
-head per (request, kv-head) where the oracle's cost allows it (all but the
-65,536-key workload, which compares every row of one head for one kv-head
-per request), and each request's first, last and padding rows.
+XCDs compare every row as well. The last row tile of a (request, kv-head)
+is mostly padding when T = N + 1 (the last node's heads): cases with its
+valid rows whole, partly padding and all padding, with one key split and
+with several, sit beside a case whose rows fill whole tiles. The full-size
+workloads run in the launch configuration the benchmark times and compare
+at least one row of every (request, kv-head, 128-row tile) unit of the
+kernel, every row of one query head per (request, kv-head) where the
+oracle's cost allows it (all but the 65,536-key workload, which compares
+every row of one head for one kv-head per request), and each request's
+first, last and padding rows.
 Device-side checks: V values beyond the fp16 range and requests whose K/V
 rows are outside the caches are reported in the status words.
 """
@@ -96,6 +100,9 @@ SMALL = [
     (2, 6, 60, 6, 100, 32, 8, [1500, 1500]),    # split, equal lengths (ties by index)
     (1, 16, 80, 8, 64, 32, 4, [4000]),          # 4 (request, kv-head) pairs: splits cut into units
     (2, 4, 40, 4, 40, 16, 2, [2500, 5000]),     # 4 pairs, ragged, longer request second
+    (1, 6, 40, 4, 63, 8, 2, [500]),             # R = 256: two full row tiles, no tail rows
+    (2, 2, 20, 2, 32, 8, 2, [300, 40]),         # 4-row last tile, all padding (7-node trees)
+    (2, 2, 20, 2, 32, 8, 2, [3000, 40]),        # the same with split keys
 ]
 
 
@@ -146,6 +153,26 @@ def test_attn_bf16_batch_beyond_xcds_all_rows():
     sel = _all_rows(B, T, Hq)
     check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, torch.bfloat16)
     assert torch.all(out[5, 17:] == 0)
+    assert np.all(st == 0), st
+
+
+def test_attn_bf16_last_tile_partly_padding():
+    """g = 1 and T = 160: a 32-row last tile past one full row tile, one
+    node per row. Request 0's tree is cut to 140 nodes, so 12 of those rows
+    are valid and 20 are padding; request 0's keys are split, request 1's
+    are not."""
+    B, L, V, K, N, Hq, Hkv, P = 2, 7, 40, 2, 159, 4, 4, [3000, 200]
+    T = N + 1
+    tree = _tree(B, L, V, K, N, seed=160)
+    assert int(tree["num_nodes"].min()) == T
+    tree["num_nodes"][0] = 140
+    tree["mask"][0, 140:] = 0
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=160)
+    note("attn bf16 last tile partly padding P=%s" % P)
+    out, offs, st = _run(q, k, v, P, tree, T)
+    sel = _all_rows(B, T, Hq)
+    check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, torch.bfloat16)
+    assert torch.all(out[0, 140:] == 0)
     assert np.all(st == 0), st
 
 
@@ -261,13 +288,14 @@ def test_attn_v_range_status(P):
         check_attn(out, _ref(q, k, v2, offs, P, tree, T, sel0), sel0, torch.bfloat16)
 
 
-def test_attn_bad_kv_rows_zero_and_flagged():
+@pytest.mark.parametrize("N", [20, 32])   # one row tile / a full tile and a 4-row one
+def test_attn_bad_kv_rows_zero_and_flagged(N):
     """Requests whose K/V rows are not inside the caches (a negative offset, a
     negative prefix, a region past the last row) read nothing: their rows are
     zeros and DDTREE_STATUS_BAD_KV is set; the valid request matches. Every
     buffer is in bounds: the device check keeps the kernel from reading the
     described rows at all."""
-    B, L, V, K, N, Hq, Hkv = 4, 4, 30, 4, 20, 32, 8
+    B, L, V, K, Hq, Hkv = 4, 4, 30, 4, 32, 8
     T = N + 1
     P = [300, 300, 300, 300]
     tree = _tree(B, L, V, K, N, seed=6)
