@@ -206,17 +206,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   const uint16_t* Vg = static_cast<const uint16_t*>(a.v);
   uint16_t* O = static_cast<uint16_t*>(a.out);
 
+  // A last row tile of at most 32 rows -- the last node's g heads when
+  // T = N + 1 -- would leave three waves on padding rows. There waves 0 and
+  // 1 take the same 32 rows, each one 32-key half of every key tile, and
+  // merge their partial results at the end; waves 2 and 3 only stage tiles.
+  const bool halves = R - tile_row0 <= kRowsPerWave;
+
   // rows of this lane: query row n = lane % 32 of wave w
   const int gq = lane >> 5;           // lane group (0/1)
   const int n = lane & 31;
-  const int row = tile_row0 + w * kRowsPerWave + n;
+  const int row = tile_row0 + (halves ? 0 : w * kRowsPerWave) + n;
   const int node = row / g;
   const int head = hk * g + (row - node * g);
   const bool row_valid = row < nvalid_rows;
 
   if (tile_row0 >= nvalid_rows) {
     // padding rows only: split 0 writes the zeros
-    if (z == 0 && row < R) {
+    if (z == 0 && row < R && (!halves || w == 0)) {
       uint16_t* o = O + (((size_t)b * T + node) * a.Hq + head) * kD;
       for (int c = gq; c < kD / 8; c += 2) reinterpret_cast<uint4*>(o)[c] = make_uint4(0, 0, 0, 0);
     }
@@ -333,6 +339,92 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   auto load_mword = [&](int t) __attribute__((always_inline)) -> uint64_t {
     return (t >= np && row_valid) ? mrow[t - np] : 0ull;
   };
+  // V fragments (A operand of O^T += V^T P^T) of 32-key half kb of the tile in vl
+  auto read_v = [&](const unsigned char* vl, int kb, halfx8 (&vf)[4][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int kofs = (32 * kb + 16 * hf) * 256;
+        const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][0] + kofs));
+        const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][1] + kofs));
+        vf[db][hf] = __builtin_bit_cast(halfx8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      }
+  };
+  // Scores of 32-key half kb masked to the allowed keys (tree tiles and the
+  // ragged last prefix tile). Query rows past num_nodes need no masking:
+  // their scores never reach a valid row and their outputs are written as
+  // zeros.
+  auto apply_mask = [&](floatx16& s, uint64_t allow, int kb) __attribute__((always_inline)) {
+    // register v holds key 32 kb + 8 gq + v (v < 8) or + 8 more (v >= 8)
+    const uint32_t sh = 32 * kb + 8 * gq;
+    const uint32_t bits = (uint32_t)((allow >> sh) & 0xFFull) | ((uint32_t)((allow >> (sh + 16)) & 0xFFull) << 8);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = ((bits >> v) & 1u) ? s[v] : -INFINITY;
+  };
+  // Weights p = 2^(s c - m_run) of one half against the row's reference
+  // m_run, taken without a maximum. The reference is an exact running
+  // maximum of the row's scores, re-taken only where it has to move: on a
+  // half tile whose weights sum to more than 2^15 (or to no finite value),
+  // and while a row has met no key (m_run = -inf). Weights then stay below
+  // 2^15, inside fp16; O and l share the reference, so O / l is unchanged.
+  // The row sum l adds the fp16 weights that enter the P.V product
+  // (v_dot2_f32_f16 with fp32 accumulation).
+  auto probs = [&](const floatx16& s, halfx8 (&pf)[2]) __attribute__((always_inline)) -> float {
+    const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
+    float ps = 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      halfx2 h2[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        floatx2 pr;
+        pr[0] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + 2 * e2], c_log2, neg_m));
+        pr[1] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + 2 * e2 + 1], c_log2, neg_m));
+        h2[e2] = __builtin_convertvector(pr, halfx2);
+        ps = __builtin_amdgcn_fdot2(h2[e2], halfx2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
+      }
+      pf[hf] = halfx8{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
+    }
+    return ps;
+  };
+  // the rare path: the half tile's exact maximum becomes the reference
+  // where it is larger, O and l are rescaled, the weights recomputed
+  auto settle = [&](const floatx16& s, halfx8 (&pf)[2], float& ps) __attribute__((always_inline)) {
+    if (__ballot(m_run == -INFINITY || !(ps <= 32768.0f)) == 0ull) return;
+    float hmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) hmax = fmaxf(hmax, s[v]);
+    hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+    const float m_new = fmaxf(m_run, hmax * c_log2);
+    const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+    ps = probs(s, pf);
+  };
+  auto pv = [&](const halfx8 (&vfr)[4][2], const halfx8 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
+  };
+  // allowed keys of this lane's query row in tile t: in range and (tree
+  // tiles) ancestors
+  auto tile_allow = [&](int t, uint64_t mword, bool* need_mask) __attribute__((always_inline)) -> uint64_t {
+    int base, nvalid;
+    tile_rows(t, &base, &nvalid);
+    const bool tree_tile = t >= np;
+    *need_mask = tree_tile || nvalid < kKeys;
+    uint64_t allow = nvalid >= kKeys ? ~0ull : ((1ull << nvalid) - 1ull);
+    if (tree_tile) allow &= mword;
+    return allow;
+  };
+
   // One key tile from LDS (kl, vl: the tile's K and V buffers; nk, nv: the
   // other buffers, where the next tile's DMA goes when has_next). Both
   // 32-key halves of S^T are computed first (two independent MFMA chains);
@@ -343,13 +435,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   auto tile_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl,
                        unsigned char* nk, unsigned char* nv, bool has_next)
       __attribute__((always_inline)) {
-    int base, nvalid;
-    tile_rows(t, &base, &nvalid);
-    const bool tree_tile = t >= np;
-    const bool need_mask = tree_tile || nvalid < kKeys;
-    // allowed keys of this lane's query row: in range and (tree tiles) ancestors
-    uint64_t allow = nvalid >= kKeys ? ~0ull : ((1ull << nvalid) - 1ull);
-    if (tree_tile) allow &= mword;
+    bool need_mask;
+    const uint64_t allow = tile_allow(t, mword, &need_mask);
 
     // ---- S^T = K Q^T for keys 0..31 (sc[0]) and 32..63 (sc[1])
     floatx16 sc[2];
@@ -382,123 +469,115 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       mword_next = load_mword(t + 1);
     }
     // V fragments of the first half, read while the scores are computed
-    auto read_v = [&](int kb, halfx8 (&vf)[4][2]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int kofs = (32 * kb + 16 * hf) * 256;
-          const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][0] + kofs));
-          const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][1] + kofs));
-          vf[db][hf] = __builtin_bit_cast(halfx8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-        }
-    };
     halfx8 vf[4][2];
-    read_v(0, vf);
-
-    // ---- mask (tree tiles and the ragged last prefix tile only). Query rows
-    // past num_nodes need no masking: their scores never reach a valid row
-    // and their outputs are written as zeros.
+    read_v(vl, 0, vf);
     if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // register v holds key 32 kb + 8 gq + v (v < 8) or + 8 more (v >= 8)
-        const uint32_t sh = 32 * kb + 8 * gq;
-        const uint32_t bits = (uint32_t)((allow >> sh) & 0xFFull) | ((uint32_t)((allow >> (sh + 16)) & 0xFFull) << 8);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sc[kb][v] = ((bits >> v) & 1u) ? sc[kb][v] : -INFINITY;
-      }
+      apply_mask(sc[0], allow, 0);
+      apply_mask(sc[1], allow, 1);
     }
-    // Weights p = 2^(s c - m_run) against the row's reference m_run, taken
-    // without a maximum. The reference is an exact running maximum of the
-    // row's scores, re-taken only where it has to move: on a half tile whose
-    // weights sum to more than 2^15 (or to no finite value), and while a row
-    // has met no key (m_run = -inf). Weights then stay below 2^15, inside
-    // fp16; O and l share the reference, so O / l is unchanged. The row sum
-    // l adds the fp16 weights that enter the P.V product (v_dot2_f32_f16
-    // with fp32 accumulation).
-    auto probs = [&](int kb, halfx8 (&pf)[2]) __attribute__((always_inline)) -> float {
-      const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
-      float ps = 0.0f;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        halfx2 h2[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          floatx2 pr;
-          pr[0] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2], c_log2, neg_m));
-          pr[1] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * hf + 2 * e2 + 1], c_log2, neg_m));
-          h2[e2] = __builtin_convertvector(pr, halfx2);
-          ps = __builtin_amdgcn_fdot2(h2[e2], halfx2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
-        }
-        pf[hf] = halfx8{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
-      }
-      return ps;
-    };
-    // the rare path: the half tile's exact maximum becomes the reference
-    // where it is larger, O and l are rescaled, the weights recomputed
-    auto settle = [&](int kb, halfx8 (&pf)[2], float& ps) __attribute__((always_inline)) {
-      if (__ballot(m_run == -INFINITY || !(ps <= 32768.0f)) == 0ull) return;
-      float hmax = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) hmax = fmaxf(hmax, sc[kb][v]);
-      hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-      const float m_new = fmaxf(m_run, hmax * c_log2);
-      const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-      ps = probs(kb, pf);
-    };
-    auto pv = [&](const halfx8 (&vfr)[4][2], const halfx8 (&pf)[2]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
-    };
     halfx8 pf0[2];
-    float ps0 = probs(0, pf0);
-    settle(0, pf0, ps0);
+    float ps0 = probs(sc[0], pf0);
+    settle(sc[0], pf0, ps0);
     pv(vf, pf0);
     l_run += ps0;
     halfx8 vf1[4][2];
-    read_v(1, vf1);
+    read_v(vl, 1, vf1);
     halfx8 pf1[2];
-    float ps1 = probs(1, pf1);
-    settle(1, pf1, ps1);
+    float ps1 = probs(sc[1], pf1);
+    settle(sc[1], pf1, ps1);
     pv(vf1, pf1);
     l_run += ps1;
+  };
+  // The same tile when waves 0 and 1 share 32 rows (halves): wave w takes
+  // the keys of half w; waves 2 and 3 only stage their part of the next tile.
+  auto half_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl,
+                       unsigned char* nk, unsigned char* nv, bool has_next)
+      __attribute__((always_inline)) {
+    if (w >= 2) {
+      if (has_next) dma_tile(t + 1, nk, nv);
+      return;
+    }
+    bool need_mask;
+    const uint64_t allow = tile_allow(t, mword, &need_mask);
+    floatx16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+    bf16x8 kf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + w * 32 * 256);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+    if (has_next) {
+      dma_tile(t + 1, nk, nv);
+      mword_next = load_mword(t + 1);
+    }
+    halfx8 vf[4][2];
+    read_v(vl, w, vf);
+    if (need_mask) apply_mask(s, allow, w);
+    halfx8 pf[2];
+    float ps = probs(s, pf);
+    settle(s, pf, ps);
+    pv(vf, pf);
+    l_run += ps;
   };
 
   // Tiles alternate between two LDS buffers (static, so that the compiler
   // sees the DMA into one buffer and the reads of the other as disjoint):
   // while tile t is computed from one buffer, tile t+1 lands in the other.
-  if (t_begin < t_end) {
-    dma_tile(t_begin, k_lds0, v_lds0);
-    mword_next = load_mword(t_begin);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  if (t_begin < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
-  __syncthreads();
-  for (int t = t_begin; t < t_end; t += 2) {
-    {
-      const uint64_t mword = mword_next;
-      tile_body(t, mword, k_lds0, v_lds0, k_lds1, v_lds1, t + 1 < t_end);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
-      if (t + 1 < t_end && !pre) v_tile_to_f16(v_lds1, w, lane);
-      __syncthreads();
+  auto run_tiles = [&](auto&& body) __attribute__((always_inline)) {
+    if (t_begin < t_end) {
+      dma_tile(t_begin, k_lds0, v_lds0);
+      mword_next = load_mword(t_begin);
     }
-    if (t + 1 < t_end) {
-      const uint64_t mword = mword_next;
-      tile_body(t + 1, mword, k_lds1, v_lds1, k_lds0, v_lds0, t + 2 < t_end);
-      __builtin_amdgcn_s_waitcnt(0);
-      if (t + 2 < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
-      __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);
+    if (t_begin < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
+    __syncthreads();
+    for (int t = t_begin; t < t_end; t += 2) {
+      {
+        const uint64_t mword = mword_next;
+        body(t, mword, k_lds0, v_lds0, k_lds1, v_lds1, t + 1 < t_end);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
+        if (t + 1 < t_end && !pre) v_tile_to_f16(v_lds1, w, lane);
+        __syncthreads();
+      }
+      if (t + 1 < t_end) {
+        const uint64_t mword = mword_next;
+        body(t + 1, mword, k_lds1, v_lds1, k_lds0, v_lds0, t + 2 < t_end);
+        __builtin_amdgcn_s_waitcnt(0);
+        if (t + 2 < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
+        __syncthreads();
+      }
     }
+  };
+  if (!halves) {
+    run_tiles(tile_body);
+  } else {
+    run_tiles(half_body);
+    // wave 1 hands its (m, l, O) to wave 0 through the idle K buffer; each
+    // lane's rows are the same in both waves, so the merge is per lane:
+    // M = max(m0, m1), O = O0 2^(m0 - M) + O1 2^(m1 - M), l likewise
+    float* xo = reinterpret_cast<float*>(k_lds0);  // 64 values per lane: 16 KB
+    float* xm = reinterpret_cast<float*>(v_lds0);
+    if (w == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xo[(db * 16 + v) * 64 + lane] = acc_o[db][v];
+      xm[lane] = m_run;
+      xm[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const float m1 = xm[lane], l1 = xm[64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mm);
+    const float a1 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc_o[db][v] = acc_o[db][v] * a0 + xo[(db * 16 + v) * 64 + lane] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = mm;
   }
 
   const float l_row = l_run + __shfl_xor(l_run, 32, 64);

@@ -11,9 +11,10 @@ the split-KV path with requests of different lengths and with fewer
 (request, kv-head) pairs than XCDs); the largest tree (T = 1025, split keys,
 ragged prefixes and a ragged last row tile) and a batch of more requests than
 XCDs compare every row as well. The last row tile of a (request, kv-head)
-is mostly padding when T = N + 1 (the last node's heads): cases with its
-valid rows whole, partly padding and all padding, with one key split and
-with several, sit beside a case whose rows fill whole tiles. The full-size
+is mostly padding when T = N + 1 (the last node's heads); a tile of at most
+32 rows has two waves take its keys by 32-key halves and merge: cases with
+its valid rows whole, partly padding and all padding, with one key split
+and with several, sit beside a case whose rows fill whole tiles. The full-size
 workloads run in the launch configuration the benchmark times and compare
 at least one row of every (request, kv-head, 128-row tile) unit of the
 kernel, every row of one query head per (request, kv-head) where the
