@@ -18,11 +18,13 @@
 // (lane = query row), online softmax in fp32 (exp2 domain) against a
 // running reference that moves only when the weights would leave the fp16
 // range, O^T += V^T P^T on v_mfma_f32_32x32x16_f16: each V tile is converted
-// to fp16 in LDS once (every wave converts the rows it staged), and P enters
-// as fp16 (2^-12 relative per weight, against 2^-9 for bf16 weights).
-// The key tile list is prefix tiles then tree tiles (mask applied); long
-// lists are split across workgroups and merged by a second kernel
-// (log-sum-exp weights).
+// to fp16 in LDS once (every wave converts the rows it staged) -- or, when
+// many row tiles read every V tile, a pass of its own (k_v_f16) converts the
+// request's V rows once before the main kernel -- and P enters as fp16
+// (2^-11 relative per weight, against 2^-8 for bf16 weights). A row tile of
+// at most 32 rows has two waves take its keys by 32-key halves. The key tile
+// list is prefix tiles then tree tiles (mask applied); long lists are split
+// across workgroups and merged by a second kernel (log-sum-exp weights).
 //
 // f32 (k_attn_simple): one thread per query row, fp32 throughout.
 #include "ddtree_device.h"

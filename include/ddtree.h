@@ -192,7 +192,7 @@ int ddtree_mask(const int32_t *parents, const int32_t *num_nodes, int batch, int
  * not an error of the call.
  *
  * bf16: q.k on bf16 MFMA with fp32 accumulation; softmax in fp32; the
- * P.V product on fp16 MFMA (weights rounded to fp16, 2^-12 relative; V
+ * P.V product on fp16 MFMA (weights rounded to fp16, 2^-11 relative; V
  * converted to fp16, exact for |v| in [2^-14, 65280] -- the largest bf16
  * value below the fp16 limit --, smaller values rounded to fp16 subnormals).
  * A bf16 V value of magnitude 65536 or more (or a non-finite one) in the
