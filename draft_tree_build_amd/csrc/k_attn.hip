@@ -20,8 +20,10 @@
 // range, O^T += V^T P^T on v_mfma_f32_32x32x16_f16: each V tile is converted
 // to fp16 in LDS once (every wave converts the rows it staged) -- or, when
 // many row tiles read every V tile, a pass of its own (k_v_f16) converts the
-// request's V rows once before the main kernel -- and P enters as fp16
-// (2^-11 relative per weight, against 2^-8 for bf16 weights). A row tile of
+// request's V tiles once before the main kernel and stores them in the order
+// the MFMA operands are read, so that the main kernel copies each tile as
+// one block and reads a V fragment with one 16-byte load -- and P enters as
+// fp16 (2^-11 relative per weight, against 2^-8 for bf16 weights). A row tile of
 // at most 32 rows has two waves take its keys by 32-key halves. The key tile
 // list is prefix tiles then tree tiles (mask applied); long lists are split
 // across workgroups and merged by a second kernel (log-sum-exp weights).
@@ -56,6 +58,26 @@ typedef short short8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + ((chunk ^ swz(row)) << 4); }
+
+// V fragments, the A operand of O^T += V^T P^T on v_mfma_f32_32x32x16_f16:
+// for dims 32 db .. + 31 and keys 16 s .. + 15 of a tile, lane l holds
+// dim 32 db + l % 32 and keys 16 s + 8 (l / 32) + 0..7. From a row-major
+// tile they come out transposed through two ds_read_b64_tr_b16 (4 keys
+// each): 16-lane group G holds dims 32 db + 16 (G % 2) + 0..15 and keys
+// 16 s + 8 (G / 2) + 0..7; read rd covers keys + 4 rd .. + 3, lane i of the
+// group pointing at key + i / 4, dims + 4 (i % 4) .. + 3. v_tr_off is that
+// pointer's byte offset for keys 16 s = 0; key step s adds s * 16 rows.
+__device__ __forceinline__ int v_tr_off(int lane, int db, int rd) {
+  const int G = lane >> 4, ti = lane & 15;
+  const int row = 8 * (G >> 1) + 4 * rd + (ti >> 2);
+  const int dim = 32 * db + 16 * (G & 1) + 4 * (ti & 3);
+  return tile_off(row, dim >> 3) + ((dim & 7) << 1);
+}
+__device__ __forceinline__ halfx8 v_frag_tr(const unsigned char* p0, const unsigned char* p1) {
+  const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+  const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+  return __builtin_bit_cast(halfx8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+}
 
 // bf16 -> fp16 in place for the four 1 KB blocks of a V tile that wave w
 // staged (bytes 4096 w .. 4096 w + 4095; 16 bytes per lane and block). The
@@ -111,30 +133,57 @@ struct AttnSplit {
 constexpr int kPreconvMinRowTiles = 16;
 constexpr size_t kPreconvMaxBytes = (size_t)4 << 30;
 
-// fp16 copy of the V rows the verify reads: request b's rows [0, P_b + T)
-// at vh + (b * (max_prefix_len + T) + row) * Hkv * 128, the same rounding as
-// v_tile_to_f16. Requests outside the caches or with P_b > max_prefix_len
-// are skipped (the main kernel converts those itself). Grid: x = chunks of
-// 2048 16-byte vectors, y = request.
+// Key tiles of one (request, kv-head) in the fp16 V copy: the prefix tiles
+// of the longest prefix, then the tree tiles.
+__host__ __device__ inline int vh_tiles(int T, int max_prefix_len) {
+  return (int)(((long long)max_prefix_len + kKeys - 1) / kKeys + ((long long)T + kKeys - 1) / kKeys);
+}
+
+// fp16 copy of the V tiles the verify reads, with the same rounding as
+// v_tile_to_f16, laid out in fragment order: key tile t of (request b,
+// kv-head h) is 16 KB at vh + ((b * Hkv + h) * vh_tiles + t) * 16384 bytes
+// -- t numbers the tiles as the main kernel does (prefix tiles, then tree
+// tiles from key P_b on) -- and holds the 16 V fragments of the tile, key
+// step s = 0..3 and dim block db = 0..3 at (4 s + db) * 1024, lane l's 16
+// bytes at 16 l. The main kernel thus stages a tile with one contiguous
+// copy and reads each fragment with one ds_read_b128 free of bank
+// conflicts. Keys a tile does not hold (past the prefix, past num_nodes)
+// are zeros. Requests outside the caches or with P_b > max_prefix_len are
+// skipped (the main kernel converts those itself). One workgroup per tile;
+// grid: x = tile, y = kv-head, z = request.
 __global__ __launch_bounds__(256) void k_v_f16(AttnArgs a, uint16_t* vh) {
-  const int b = (int)blockIdx.y;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kTileBytes];
+  const int t = (int)blockIdx.x, hk = (int)blockIdx.y, b = (int)blockIdx.z;
   const int64_t kv0 = a.kv_offsets[b];
   const int P = a.prefix_lens[b];
-  if (!kv_in_range(kv0, P, a.T, a.total_rows) || P > a.max_prefix_len) return;
-  const int64_t vecs = ((int64_t)P + a.T) * a.Hkv * (kD / 8);
-  const int64_t base = (int64_t)blockIdx.x * 2048;
-  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + kv0 * a.Hkv * kD);
-  uint4* dst = reinterpret_cast<uint4*>(vh + (size_t)b * (a.max_prefix_len + a.T) * a.Hkv * kD);
-  uint4 u[8];
+  const int T = a.T;
+  if (!kv_in_range(kv0, P, T, a.total_rows) || P > a.max_prefix_len) return;
+  const int np = (P + kKeys - 1) / kKeys;
+  if (t >= np + (T + kKeys - 1) / kKeys) return;
+  int base, nvalid;
+  if (t < np) {
+    base = t * kKeys;
+    nvalid = min(kKeys, P - base);
+  } else {
+    const int tt = t - np;
+    base = P + tt * kKeys;
+    nvalid = min(kKeys, min(max(a.num_nodes[b], 0), T) - tt * kKeys);
+  }
+  // rows base .. base + nvalid - 1 lie inside the request's P_b + T rows
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(a.v) +
+                             ((size_t)(kv0 + base) * a.Hkv + hk) * (kD * 2);
+  const size_t row_bytes = (size_t)a.Hkv * kD * 2;
+  // row-major, swizzled, converted: wave w takes rows 16 w .. 16 w + 15
+  uint4 u[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t i = base + j * 256 + threadIdx.x;
-    u[j] = i < vecs ? src[i] : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * (4 * w + j) + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r);
+    u[j] = r < nvalid ? *reinterpret_cast<const uint4*>(src + r * row_bytes + c * 16) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t i = base + j * 256 + threadIdx.x;
-    if (i >= vecs) break;
+  for (int j = 0; j < 4; ++j) {
     const uint32_t in[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
     uint32_t o[4];
 #pragma unroll
@@ -142,11 +191,26 @@ __global__ __launch_bounds__(256) void k_v_f16(AttnArgs a, uint16_t* vh) {
       const floatx2 f = {__uint_as_float(in[q] << 16), __uint_as_float(in[q] & 0xFFFF0000u)};
       o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, halfx2));
     }
-    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(lds + (4 * w + j) * 1024 + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  __syncthreads();
+  // wave w writes the fragments of key step s = w
+  unsigned char* dst = reinterpret_cast<unsigned char*>(vh) +
+                       (((size_t)b * a.Hkv + hk) * vh_tiles(T, a.max_prefix_len) + t) * kTileBytes;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const unsigned char* p = lds + w * 16 * 256;
+    const halfx8 f = v_frag_tr(p + v_tr_off(lane, db, 0), p + v_tr_off(lane, db, 1));
+    *reinterpret_cast<halfx8*>(dst + (4 * w + db) * 1024 + 16 * lane) = f;
   }
 }
 
 constexpr int kXcds = 8;
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 // One workgroup = 128 query rows of one (request, kv-head) over one range of
 // key tiles. Grid: 1-D, XCD-aware -- consecutive workgroup ids go to
@@ -240,399 +304,409 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
   const int per = (ntiles + nsplit - 1) / nsplit;
   const int t_begin = min(z * per, ntiles), t_end = min(t_begin + per, ntiles);
   const size_t kv0 = (size_t)kv0s;
-  // V tiles come converted to fp16 from k_v_f16 when it ran for this request
-  const bool pre = vh != nullptr && P <= a.max_prefix_len;
-  const size_t vrow0 = (size_t)b * ((size_t)a.max_prefix_len + T);
-  const int W = (T + 63) >> 6;
-  const float c_log2 = a.scale * kLog2e;
+  // V tiles come converted to fp16, in fragment order, from k_v_f16 when it
+  // ran for this request. The rest of the kernel is compiled once for each
+  // case, so that neither carries a branch on it inside the tile loop
+  // (measured: such branches cost 6-10% of the verify, since they cut the
+  // schedule of LDS reads, exponentials and MFMAs into pieces).
+  auto rest = [&](auto pre_tag) __attribute__((always_inline)) {
+    constexpr bool pre = decltype(pre_tag)::value;
+    const unsigned char* vh_bh =
+        pre ? reinterpret_cast<const unsigned char*>(vh) +
+                  ((size_t)b * a.Hkv + hk) * vh_tiles(T, a.max_prefix_len) * kTileBytes
+            : nullptr;
+    const int W = (T + 63) >> 6;
+    const float c_log2 = a.scale * kLog2e;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): dims 16 ks + 8 gq + 0..7
-  bf16x8 qf[8];
-  {
-    const uint16_t* qp = Q + (((size_t)b * T + node) * a.Hq + head) * kD + 8 * gq;
+    // ---- Q fragments (B operand of S^T = K Q^T): dims 16 ks + 8 gq + 0..7
+    bf16x8 qf[8];
+    {
+      const uint16_t* qp = Q + (((size_t)b * T + node) * a.Hq + head) * kD + 8 * gq;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 u = row_valid ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8, u);
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 u = row_valid ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+        qf[ks] = __builtin_bit_cast(bf16x8, u);
+      }
     }
-  }
 
-  floatx16 acc_o[4];
+    floatx16 acc_o[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.0f;
-  // padding rows (no keys, zero Q) take a finite reference from the start
-  float m_run = row_valid ? -INFINITY : 0.0f, l_run = 0.0f;
+      for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.0f;
+    // padding rows (no keys, zero Q) take a finite reference from the start
+    float m_run = row_valid ? -INFINITY : 0.0f, l_run = 0.0f;
 
-  // ---- staging by DMA: wave w moves rows 16 w .. 16 w + 15 of K and V, four
-  // 1 KB blocks each; lane i of a block writes LDS bytes 16 i of it, so it
-  // fetches row 4 blk + i / 16, logical chunk (i % 16) ^ sw(row).
-  const uint32_t row_bytes = (uint32_t)a.Hkv * kD * 2;
-  uint32_t dma_off[4];   // byte offset from the tile's first K/V row
-  int dma_row[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int blk = 4 * w + j;
-    const int r = 4 * blk + (lane >> 4);
-    const int c = (lane & 15) ^ swz(r);
-    dma_row[j] = r;
-    dma_off[j] = (uint32_t)r * row_bytes + (uint32_t)hk * (kD * 2) + (uint32_t)c * 16;
-  }
-  auto tile_rows = [&](int t, int* base, int* nvalid) __attribute__((always_inline)) {
-    if (t < np) {
-      *base = t * kKeys;
-      *nvalid = min(kKeys, P - t * kKeys);
-    } else {
-      const int tt = t - np;
-      *base = P + tt * kKeys;
-      *nvalid = min(kKeys, nn - tt * kKeys);
-    }
-  };
-  auto dma_tile = [&](int t, unsigned char* kbuf, unsigned char* vbuf) __attribute__((always_inline)) {
-    int base, nvalid;
-    tile_rows(t, &base, &nvalid);
-    // every key row of the request is inside the caches (kv_in_range) and a
-    // tile holds at least one valid key
-    const size_t tb = (kv0 + (size_t)base) * row_bytes;
-    const unsigned char* kt = reinterpret_cast<const unsigned char*>(Kg) + tb;
-    const unsigned char* vt =
-        pre ? reinterpret_cast<const unsigned char*>(vh) + (vrow0 + (size_t)base) * row_bytes
-            : reinterpret_cast<const unsigned char*>(Vg) + tb;
+    // ---- staging by DMA: wave w moves rows 16 w .. 16 w + 15 of K and V, four
+    // 1 KB blocks each; lane i of a block writes LDS bytes 16 i of it, so it
+    // fetches row 4 blk + i / 16, logical chunk (i % 16) ^ sw(row).
+    const uint32_t row_bytes = (uint32_t)a.Hkv * kD * 2;
+    uint32_t dma_off[4];   // byte offset from the tile's first K/V row
+    int dma_row[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // rows past the tile's nvalid keys re-read the tile's first row: their
-      // scores are masked (allow covers keys < nvalid only), so they only
-      // ever meet zero weights
-      const uint32_t off = dma_row[j] < nvalid ? dma_off[j] : dma_off[j] - (uint32_t)dma_row[j] * row_bytes;
-      unsigned char* kd = kbuf + (4 * w + j) * 1024;
-      unsigned char* vd = vbuf + (4 * w + j) * 1024;
-      __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt + off, (__attribute__((address_space(3))) void*)vd, 16, 0, 0);
+      const int blk = 4 * w + j;
+      const int r = 4 * blk + (lane >> 4);
+      const int c = (lane & 15) ^ swz(r);
+      dma_row[j] = r;
+      dma_off[j] = (uint32_t)r * row_bytes + (uint32_t)hk * (kD * 2) + (uint32_t)c * 16;
     }
-  };
+    auto tile_rows = [&](int t, int* base, int* nvalid) __attribute__((always_inline)) {
+      if (t < np) {
+        *base = t * kKeys;
+        *nvalid = min(kKeys, P - t * kKeys);
+      } else {
+        const int tt = t - np;
+        *base = P + tt * kKeys;
+        *nvalid = min(kKeys, nn - tt * kKeys);
+      }
+    };
+    auto dma_tile = [&](int t, unsigned char* kbuf, unsigned char* vbuf) __attribute__((always_inline)) {
+      int base, nvalid;
+      tile_rows(t, &base, &nvalid);
+      // every key row of the request is inside the caches (kv_in_range) and a
+      // tile holds at least one valid key
+      const size_t tb = (kv0 + (size_t)base) * row_bytes;
+      const unsigned char* kt = reinterpret_cast<const unsigned char*>(Kg) + tb;
+      const unsigned char* vt = reinterpret_cast<const unsigned char*>(Vg) + tb;
+      // the fp16 copy's tile is one contiguous 16 KB block, copied as it is
+      const unsigned char* vp = pre ? vh_bh + (size_t)t * kTileBytes + (4 * w) * 1024 + 16 * lane : nullptr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // rows past the tile's nvalid keys re-read the tile's first row: their
+        // scores are masked (allow covers keys < nvalid only), so they only
+        // ever meet zero weights
+        const uint32_t off = dma_row[j] < nvalid ? dma_off[j] : dma_off[j] - (uint32_t)dma_row[j] * row_bytes;
+        unsigned char* kd = kbuf + (4 * w + j) * 1024;
+        unsigned char* vd = vbuf + (4 * w + j) * 1024;
+        __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(pre ? vp + j * 1024 : vt + off,
+                                         (__attribute__((address_space(3))) void*)vd, 16, 0, 0);
+      }
+    };
 
-  // ---- fragment addresses (bytes within a tile)
-  // K (A operand of S^T): lane row m -> key pi(m), chosen so that lane group
-  // gq's score registers v = 0..7 hold keys 8 gq + v and v = 8..15 hold keys
-  // 16 + 8 gq + (v - 8) of each 32-key half; dims 16 ks + 8 gq + 0..7.
-  const int m_a = lane & 31;
-  const int pi_m = 8 * ((m_a >> 2) & 1) + 16 * (m_a >> 4) + 4 * ((m_a >> 3) & 1) + (m_a & 3);
-  int kfrag[8];
+    // ---- fragment addresses (bytes within a tile)
+    // K (A operand of S^T): lane row m -> key pi(m), chosen so that lane group
+    // gq's score registers v = 0..7 hold keys 8 gq + v and v = 8..15 hold keys
+    // 16 + 8 gq + (v - 8) of each 32-key half; dims 16 ks + 8 gq + 0..7.
+    const int m_a = lane & 31;
+    const int pi_m = 8 * ((m_a >> 2) & 1) + 16 * (m_a >> 4) + 4 * ((m_a >> 3) & 1) + (m_a & 3);
+    int kfrag[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) kfrag[ks] = tile_off(pi_m, 2 * ks + gq);
-  // V (A operand of O^T = V^T P^T, read transposed): 16-lane group G holds
-  // dims 32 db + 16 (G % 2) + t and keys 16 hf + 8 (G / 2) + 0..7 of a half;
-  // transpose-read rd covers keys + 4 rd .. + 3, lane i of the group pointing
-  // at row + i / 4, dims + 4 (i % 4) .. + 3.
-  const int G = lane >> 4, ti = lane & 15;
-  int vfrag[4][2];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int row = 8 * (G >> 1) + 4 * rd + (ti >> 2);     // + 32 kb + 16 hf (keep sw)
-      const int dim = 32 * db + 16 * (G & 1) + 4 * (ti & 3);
-      vfrag[db][rd] = tile_off(row, dim >> 3) + ((dim & 7) << 1);
-    }
-
-  // mask word of this lane's query row for tree tile t (prefetched with the tile)
-  const uint64_t* mrow = a.mask + ((size_t)b * T + node) * W;
-  auto load_mword = [&](int t) __attribute__((always_inline)) -> uint64_t {
-    return (t >= np && row_valid) ? mrow[t - np] : 0ull;
-  };
-  // V fragments (A operand of O^T += V^T P^T) of 32-key half kb of the tile in vl
-  auto read_v = [&](const unsigned char* vl, int kb, halfx8 (&vf)[4][2]) __attribute__((always_inline)) {
+    for (int ks = 0; ks < 8; ++ks) kfrag[ks] = tile_off(pi_m, 2 * ks + gq);
+    // V fragments from a row-major tile (key step 0; see v_tr_off)
+    int vfrag[4][2];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int kofs = (32 * kb + 16 * hf) * 256;
-        const v4s v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][0] + kofs));
-        const v4s v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vl + vfrag[db][1] + kofs));
-        vf[db][hf] = __builtin_bit_cast(halfx8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-      }
-  };
-  // Scores of 32-key half kb masked to the allowed keys (tree tiles and the
-  // ragged last prefix tile). Query rows past num_nodes need no masking:
-  // their scores never reach a valid row and their outputs are written as
-  // zeros.
-  auto apply_mask = [&](floatx16& s, uint64_t allow, int kb) __attribute__((always_inline)) {
-    // register v holds key 32 kb + 8 gq + v (v < 8) or + 8 more (v >= 8)
-    const uint32_t sh = 32 * kb + 8 * gq;
-    const uint32_t bits = (uint32_t)((allow >> sh) & 0xFFull) | ((uint32_t)((allow >> (sh + 16)) & 0xFFull) << 8);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = ((bits >> v) & 1u) ? s[v] : -INFINITY;
-  };
-  // Weights p = 2^(s c - m_run) of one half against the row's reference
-  // m_run, taken without a maximum. The reference is an exact running
-  // maximum of the row's scores, re-taken only where it has to move: on a
-  // half tile whose weights sum to more than 2^15 (or to no finite value),
-  // and while a row has met no key (m_run = -inf). Weights then stay below
-  // 2^15, inside fp16; O and l share the reference, so O / l is unchanged.
-  // The row sum l adds the fp16 weights that enter the P.V product
-  // (v_dot2_f32_f16 with fp32 accumulation).
-  auto probs = [&](const floatx16& s, halfx8 (&pf)[2]) __attribute__((always_inline)) -> float {
-    const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
-    float ps = 0.0f;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      halfx2 h2[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        floatx2 pr;
-        pr[0] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + 2 * e2], c_log2, neg_m));
-        pr[1] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + 2 * e2 + 1], c_log2, neg_m));
-        h2[e2] = __builtin_convertvector(pr, halfx2);
-        ps = __builtin_amdgcn_fdot2(h2[e2], halfx2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
-      }
-      pf[hf] = halfx8{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
-    }
-    return ps;
-  };
-  // the rare path: the half tile's exact maximum becomes the reference
-  // where it is larger, O and l are rescaled, the weights recomputed
-  auto settle = [&](const floatx16& s, halfx8 (&pf)[2], float& ps) __attribute__((always_inline)) {
-    if (__ballot(m_run == -INFINITY || !(ps <= 32768.0f)) == 0ull) return;
-    float hmax = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) hmax = fmaxf(hmax, s[v]);
-    hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-    const float m_new = fmaxf(m_run, hmax * c_log2);
-    const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
-    l_run *= alpha;
-    m_run = m_new;
-    ps = probs(s, pf);
-  };
-  auto pv = [&](const halfx8 (&vfr)[4][2], const halfx8 (&pf)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
-  };
-  // allowed keys of this lane's query row in tile t: in range and (tree
-  // tiles) ancestors
-  auto tile_allow = [&](int t, uint64_t mword, bool* need_mask) __attribute__((always_inline)) -> uint64_t {
-    int base, nvalid;
-    tile_rows(t, &base, &nvalid);
-    const bool tree_tile = t >= np;
-    *need_mask = tree_tile || nvalid < kKeys;
-    uint64_t allow = nvalid >= kKeys ? ~0ull : ((1ull << nvalid) - 1ull);
-    if (tree_tile) allow &= mword;
-    return allow;
-  };
+      for (int rd = 0; rd < 2; ++rd) vfrag[db][rd] = v_tr_off(lane, db, rd);
 
-  // One key tile from LDS (kl, vl: the tile's K and V buffers; nk, nv: the
-  // other buffers, where the next tile's DMA goes when has_next). Both
-  // 32-key halves of S^T are computed first (two independent MFMA chains);
-  // the weights of each half are then taken against the row's running
-  // reference, and the exponentials of the second half run on the VALU
-  // while the first half's O^T += V^T P^T products occupy the matrix core.
-  uint64_t mword_next = 0;
-  auto tile_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl,
-                       unsigned char* nk, unsigned char* nv, bool has_next)
-      __attribute__((always_inline)) {
-    bool need_mask;
-    const uint64_t allow = tile_allow(t, mword, &need_mask);
-
-    // ---- S^T = K Q^T for keys 0..31 (sc[0]) and 32..63 (sc[1])
-    floatx16 sc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sc[kb][v] = 0.0f;
-    // K fragments read two steps ahead of their MFMAs (four in flight)
-    bf16x8 kf[8][2];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        kf[ks][kb] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + kb * 32 * 256);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kb], qf[ks], sc[kb], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    // the next tile's DMA is issued while the score MFMAs run
-    if (has_next) {
-      dma_tile(t + 1, nk, nv);
-      mword_next = load_mword(t + 1);
-    }
-    // V fragments of the first half, read while the scores are computed
-    halfx8 vf[4][2];
-    read_v(vl, 0, vf);
-    if (need_mask) {
-      apply_mask(sc[0], allow, 0);
-      apply_mask(sc[1], allow, 1);
-    }
-    halfx8 pf0[2];
-    float ps0 = probs(sc[0], pf0);
-    settle(sc[0], pf0, ps0);
-    pv(vf, pf0);
-    l_run += ps0;
-    halfx8 vf1[4][2];
-    read_v(vl, 1, vf1);
-    halfx8 pf1[2];
-    float ps1 = probs(sc[1], pf1);
-    settle(sc[1], pf1, ps1);
-    pv(vf1, pf1);
-    l_run += ps1;
-  };
-  // The same tile when waves 0 and 1 share 32 rows (halves): wave w takes
-  // the keys of half w; waves 2 and 3 only stage their part of the next tile.
-  auto half_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl,
-                       unsigned char* nk, unsigned char* nv, bool has_next)
-      __attribute__((always_inline)) {
-    if (w >= 2) {
-      if (has_next) dma_tile(t + 1, nk, nv);
-      return;
-    }
-    bool need_mask;
-    const uint64_t allow = tile_allow(t, mword, &need_mask);
-    floatx16 s;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = 0.0f;
-    bf16x8 kf[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + w * 32 * 256);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-    if (has_next) {
-      dma_tile(t + 1, nk, nv);
-      mword_next = load_mword(t + 1);
-    }
-    halfx8 vf[4][2];
-    read_v(vl, w, vf);
-    if (need_mask) apply_mask(s, allow, w);
-    halfx8 pf[2];
-    float ps = probs(s, pf);
-    settle(s, pf, ps);
-    pv(vf, pf);
-    l_run += ps;
-  };
-
-  // Tiles alternate between two LDS buffers (static, so that the compiler
-  // sees the DMA into one buffer and the reads of the other as disjoint):
-  // while tile t is computed from one buffer, tile t+1 lands in the other.
-  auto run_tiles = [&](auto&& body) __attribute__((always_inline)) {
-    if (t_begin < t_end) {
-      dma_tile(t_begin, k_lds0, v_lds0);
-      mword_next = load_mword(t_begin);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (t_begin < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
-    __syncthreads();
-    for (int t = t_begin; t < t_end; t += 2) {
-      {
-        const uint64_t mword = mword_next;
-        body(t, mword, k_lds0, v_lds0, k_lds1, v_lds1, t + 1 < t_end);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
-        if (t + 1 < t_end && !pre) v_tile_to_f16(v_lds1, w, lane);
-        __syncthreads();
-      }
-      if (t + 1 < t_end) {
-        const uint64_t mword = mword_next;
-        body(t + 1, mword, k_lds1, v_lds1, k_lds0, v_lds0, t + 2 < t_end);
-        __builtin_amdgcn_s_waitcnt(0);
-        if (t + 2 < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
-        __syncthreads();
-      }
-    }
-  };
-  if (!halves) {
-    run_tiles(tile_body);
-  } else {
-    run_tiles(half_body);
-    // wave 1 hands its (m, l, O) to wave 0 through the idle K buffer; each
-    // lane's rows are the same in both waves, so the merge is per lane:
-    // M = max(m0, m1), O = O0 2^(m0 - M) + O1 2^(m1 - M), l likewise
-    float* xo = reinterpret_cast<float*>(k_lds0);  // 64 values per lane: 16 KB
-    float* xm = reinterpret_cast<float*>(v_lds0);
-    if (w == 1) {
+    // mask word of this lane's query row for tree tile t (prefetched with the tile)
+    const uint64_t* mrow = a.mask + ((size_t)b * T + node) * W;
+    auto load_mword = [&](int t) __attribute__((always_inline)) -> uint64_t {
+      return (t >= np && row_valid) ? mrow[t - np] : 0ull;
+    };
+    // V fragments (A operand of O^T += V^T P^T) of 32-key half kb of the tile
+    // in vl: key steps s = 2 kb + hf, one 16-byte read each from a tile in
+    // fragment order, two transposed reads from a row-major one
+    auto read_v = [&](const unsigned char* vl, int kb, halfx8 (&vf)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) xo[(db * 16 + v) * 64 + lane] = acc_o[db][v];
-      xm[lane] = m_run;
-      xm[64 + lane] = l_run;
-    }
-    __syncthreads();
-    if (w != 0) return;
-    const float m1 = xm[lane], l1 = xm[64 + lane];
-    const float mm = fmaxf(m_run, m1);
-    const float a0 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mm);
-    const float a1 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+        for (int hf = 0; hf < 2; ++hf) {
+          if (pre) {
+            vf[db][hf] = *reinterpret_cast<const halfx8*>(vl + (4 * (2 * kb + hf) + db) * 1024 + 16 * lane);
+          } else {
+            const int kofs = (32 * kb + 16 * hf) * 256;
+            vf[db][hf] = v_frag_tr(vl + vfrag[db][0] + kofs, vl + vfrag[db][1] + kofs);
+          }
+        }
+    };
+    // Scores of 32-key half kb masked to the allowed keys (tree tiles and the
+    // ragged last prefix tile). Query rows past num_nodes need no masking:
+    // their scores never reach a valid row and their outputs are written as
+    // zeros.
+    auto apply_mask = [&](floatx16& s, uint64_t allow, int kb) __attribute__((always_inline)) {
+      // register v holds key 32 kb + 8 gq + v (v < 8) or + 8 more (v >= 8)
+      const uint32_t sh = 32 * kb + 8 * gq;
+      const uint32_t bits = (uint32_t)((allow >> sh) & 0xFFull) | ((uint32_t)((allow >> (sh + 16)) & 0xFFull) << 8);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int v = 0; v < 16; ++v) s[v] = ((bits >> v) & 1u) ? s[v] : -INFINITY;
+    };
+    // Weights p = 2^(s c - m_run) of one half against the row's reference
+    // m_run, taken without a maximum. The reference is an exact running
+    // maximum of the row's scores, re-taken only where it has to move: on a
+    // half tile whose weights sum to more than 2^15 (or to no finite value),
+    // and while a row has met no key (m_run = -inf). Weights then stay below
+    // 2^15, inside fp16; O and l share the reference, so O / l is unchanged.
+    // The row sum l adds the fp16 weights that enter the P.V product
+    // (v_dot2_f32_f16 with fp32 accumulation).
+    auto probs = [&](const floatx16& s, halfx8 (&pf)[2]) __attribute__((always_inline)) -> float {
+      const float neg_m = (m_run == -INFINITY) ? 0.0f : -m_run;
+      float ps = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc_o[db][v] = acc_o[db][v] * a0 + xo[(db * 16 + v) * 64 + lane] * a1;
-    l_run = l_run * a0 + l1 * a1;
-    m_run = mm;
-  }
+      for (int hf = 0; hf < 2; ++hf) {
+        halfx2 h2[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          floatx2 pr;
+          pr[0] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + 2 * e2], c_log2, neg_m));
+          pr[1] = __builtin_amdgcn_exp2f(fmaf(s[8 * hf + 2 * e2 + 1], c_log2, neg_m));
+          h2[e2] = __builtin_convertvector(pr, halfx2);
+          ps = __builtin_amdgcn_fdot2(h2[e2], halfx2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
+        }
+        pf[hf] = halfx8{h2[0][0], h2[0][1], h2[1][0], h2[1][1], h2[2][0], h2[2][1], h2[3][0], h2[3][1]};
+      }
+      return ps;
+    };
+    // the rare path: the half tile's exact maximum becomes the reference
+    // where it is larger, O and l are rescaled, the weights recomputed
+    auto settle = [&](const floatx16& s, halfx8 (&pf)[2], float& ps) __attribute__((always_inline)) {
+      if (__ballot(m_run == -INFINITY || !(ps <= 32768.0f)) == 0ull) return;
+      float hmax = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hmax = fmaxf(hmax, s[v]);
+      hmax = fmaxf(hmax, __shfl_xor(hmax, 32, 64));
+      const float m_new = fmaxf(m_run, hmax * c_log2);
+      const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      ps = probs(s, pf);
+    };
+    auto pv = [&](const halfx8 (&vfr)[4][2], const halfx8 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfr[db][hf], pf[hf], acc_o[db], 0, 0, 0);
+    };
+    // allowed keys of this lane's query row in tile t: in range and (tree
+    // tiles) ancestors
+    auto tile_allow = [&](int t, uint64_t mword, bool* need_mask) __attribute__((always_inline)) -> uint64_t {
+      int base, nvalid;
+      tile_rows(t, &base, &nvalid);
+      const bool tree_tile = t >= np;
+      *need_mask = tree_tile || nvalid < kKeys;
+      uint64_t allow = nvalid >= kKeys ? ~0ull : ((1ull << nvalid) - 1ull);
+      if (tree_tile) allow &= mword;
+      return allow;
+    };
 
-  const float l_row = l_run + __shfl_xor(l_run, 32, 64);
+    // One key tile from LDS (kl, vl: the tile's K and V buffers; nk, nv: the
+    // other buffers, where the next tile's DMA goes when has_next). Both
+    // 32-key halves of S^T are computed first (two independent MFMA chains);
+    // the weights of each half are then taken against the row's running
+    // reference, and the exponentials of the second half run on the VALU
+    // while the first half's O^T += V^T P^T products occupy the matrix core.
+    uint64_t mword_next = 0;
+    auto tile_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl,
+                         unsigned char* nk, unsigned char* nv, bool has_next)
+        __attribute__((always_inline)) {
+      bool need_mask;
+      const uint64_t allow = tile_allow(t, mword, &need_mask);
 
-  if (nsplit == 1) {
-    bool bad = false;
-    if (row < R) {
-      const float inv = (row_valid && l_row > 0.0f) ? 1.0f / l_row : 0.0f;
-      uint16_t* o = O + (((size_t)b * T + node) * a.Hq + head) * kD;
+      // ---- S^T = K Q^T for keys 0..31 (sc[0]) and 32..63 (sc[1])
+      floatx16 sc[2];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          floatx2 lo2 = {acc_o[db][4 * j] * inv, acc_o[db][4 * j + 1] * inv};
-          floatx2 hi2 = {acc_o[db][4 * j + 2] * inv, acc_o[db][4 * j + 3] * inv};
-          bad |= !__builtin_isfinite(lo2[0]) | !__builtin_isfinite(lo2[1]) |
-                 !__builtin_isfinite(hi2[0]) | !__builtin_isfinite(hi2[1]);
-          bf16x2 l2 = __builtin_convertvector(lo2, bf16x2);
-          bf16x2 h2 = __builtin_convertvector(hi2, bf16x2);
-          bf16x4 o4 = {l2[0], l2[1], h2[0], h2[1]};
-          *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * j + 4 * gq) = o4;
+        for (int v = 0; v < 16; ++v) sc[kb][v] = 0.0f;
+      // K fragments read two steps ahead of their MFMAs (four in flight)
+      bf16x8 kf[8][2];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          kf[ks][kb] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + kb * 32 * 256);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][kb], qf[ks], sc[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      // the next tile's DMA is issued while the score MFMAs run
+      if (has_next) {
+        dma_tile(t + 1, nk, nv);
+        mword_next = load_mword(t + 1);
+      }
+      // V fragments of the first half, read while the scores are computed
+      halfx8 vf[4][2];
+      read_v(vl, 0, vf);
+      if (need_mask) {
+        apply_mask(sc[0], allow, 0);
+        apply_mask(sc[1], allow, 1);
+      }
+      halfx8 pf0[2];
+      float ps0 = probs(sc[0], pf0);
+      settle(sc[0], pf0, ps0);
+      pv(vf, pf0);
+      l_run += ps0;
+      halfx8 vf1[4][2];
+      read_v(vl, 1, vf1);
+      halfx8 pf1[2];
+      float ps1 = probs(sc[1], pf1);
+      settle(sc[1], pf1, ps1);
+      pv(vf1, pf1);
+      l_run += ps1;
+    };
+    // The same tile when waves 0 and 1 share 32 rows (halves): wave w takes
+    // the keys of half w; waves 2 and 3 only stage their part of the next tile.
+    auto half_body = [&](int t, uint64_t mword, const unsigned char* kl, const unsigned char* vl,
+                         unsigned char* nk, unsigned char* nv, bool has_next)
+        __attribute__((always_inline)) {
+      if (w >= 2) {
+        if (has_next) dma_tile(t + 1, nk, nv);
+        return;
+      }
+      bool need_mask;
+      const uint64_t allow = tile_allow(t, mword, &need_mask);
+      floatx16 s;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = 0.0f;
+      bf16x8 kf[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kl + kfrag[ks] + w * 32 * 256);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+      if (has_next) {
+        dma_tile(t + 1, nk, nv);
+        mword_next = load_mword(t + 1);
+      }
+      halfx8 vf[4][2];
+      read_v(vl, w, vf);
+      if (need_mask) apply_mask(s, allow, w);
+      halfx8 pf[2];
+      float ps = probs(s, pf);
+      settle(s, pf, ps);
+      pv(vf, pf);
+      l_run += ps;
+    };
+
+    // Tiles alternate between two LDS buffers (static, so that the compiler
+    // sees the DMA into one buffer and the reads of the other as disjoint):
+    // while tile t is computed from one buffer, tile t+1 lands in the other.
+    auto run_tiles = [&](auto&& body) __attribute__((always_inline)) {
+      if (t_begin < t_end) {
+        dma_tile(t_begin, k_lds0, v_lds0);
+        mword_next = load_mword(t_begin);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (t_begin < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
+      __syncthreads();
+      for (int t = t_begin; t < t_end; t += 2) {
+        {
+          const uint64_t mword = mword_next;
+          body(t, mword, k_lds0, v_lds0, k_lds1, v_lds1, t + 1 < t_end);
+          __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
+          if (t + 1 < t_end && !pre) v_tile_to_f16(v_lds1, w, lane);
+          __syncthreads();
+        }
+        if (t + 1 < t_end) {
+          const uint64_t mword = mword_next;
+          body(t + 1, mword, k_lds1, v_lds1, k_lds0, v_lds0, t + 2 < t_end);
+          __builtin_amdgcn_s_waitcnt(0);
+          if (t + 2 < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
+          __syncthreads();
         }
       }
-    }
-    // a non-finite output (an infinite fp16 V value, or a non-finite input)
-    // is reported once per wave
-    if (__ballot(bad) != 0ull && lane == 0) set_status(a.status, b, kStatusNonfinite);
-    return;
-  }
-
-  // ---- split: write this split's partial (unnormalised O, m, l), streamed
-  // past the L2 (nontemporal): read once by the merge kernel, they would
-  // otherwise wait dirty in L2 for the end-of-kernel write-back (measured:
-  // 16.5 -> 14.9 us at a 2048-key prefix, merge 4.0 -> 4.3 us)
-  const int Rpad = row_tiles * kTileRows;
-  const size_t bh = (size_t)b * a.Hkv + hk;  // the merge reads (request, kv-head)
-  const size_t nbh = (size_t)a.batch * a.Hkv;
-  if (row_valid) {  // rows past num_nodes are zeroed by the merge, which never reads them
-    float* po = part_o + (((size_t)z * nbh + bh) * Rpad + row) * kD;
+    };
+    if (!halves) {
+      run_tiles(tile_body);
+    } else {
+      run_tiles(half_body);
+      // wave 1 hands its (m, l, O) to wave 0 through the idle K buffer; each
+      // lane's rows are the same in both waves, so the merge is per lane:
+      // M = max(m0, m1), O = O0 2^(m0 - M) + O1 2^(m1 - M), l likewise
+      float* xo = reinterpret_cast<float*>(k_lds0);  // 64 values per lane: 16 KB
+      float* xm = reinterpret_cast<float*>(v_lds0);
+      if (w == 1) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        floatx4 v4 = {acc_o[db][4 * j], acc_o[db][4 * j + 1], acc_o[db][4 * j + 2],
-                      acc_o[db][4 * j + 3]};
-        __builtin_nontemporal_store(v4, reinterpret_cast<floatx4*>(po + 32 * db + 8 * j + 4 * gq));
+          for (int v = 0; v < 16; ++v) xo[(db * 16 + v) * 64 + lane] = acc_o[db][v];
+        xm[lane] = m_run;
+        xm[64 + lane] = l_run;
       }
-    if (gq == 0) {
-      float* pm = part_ml + (((size_t)z * nbh + bh) * Rpad + row) * 2;
-      __builtin_nontemporal_store(m_run, pm);
-      __builtin_nontemporal_store(l_row, pm + 1);
+      __syncthreads();
+      if (w != 0) return;
+      const float m1 = xm[lane], l1 = xm[64 + lane];
+      const float mm = fmaxf(m_run, m1);
+      const float a0 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mm);
+      const float a1 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] = acc_o[db][v] * a0 + xo[(db * 16 + v) * 64 + lane] * a1;
+      l_run = l_run * a0 + l1 * a1;
+      m_run = mm;
     }
-  }
+
+    const float l_row = l_run + __shfl_xor(l_run, 32, 64);
+
+    if (nsplit == 1) {
+      bool bad = false;
+      if (row < R) {
+        const float inv = (row_valid && l_row > 0.0f) ? 1.0f / l_row : 0.0f;
+        uint16_t* o = O + (((size_t)b * T + node) * a.Hq + head) * kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            floatx2 lo2 = {acc_o[db][4 * j] * inv, acc_o[db][4 * j + 1] * inv};
+            floatx2 hi2 = {acc_o[db][4 * j + 2] * inv, acc_o[db][4 * j + 3] * inv};
+            bad |= !__builtin_isfinite(lo2[0]) | !__builtin_isfinite(lo2[1]) |
+                   !__builtin_isfinite(hi2[0]) | !__builtin_isfinite(hi2[1]);
+            bf16x2 l2 = __builtin_convertvector(lo2, bf16x2);
+            bf16x2 h2 = __builtin_convertvector(hi2, bf16x2);
+            bf16x4 o4 = {l2[0], l2[1], h2[0], h2[1]};
+            *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * j + 4 * gq) = o4;
+          }
+        }
+      }
+      // a non-finite output (an infinite fp16 V value, or a non-finite input)
+      // is reported once per wave
+      if (__ballot(bad) != 0ull && lane == 0) set_status(a.status, b, kStatusNonfinite);
+      return;
+    }
+
+    // ---- split: write this split's partial (unnormalised O, m, l), streamed
+    // past the L2 (nontemporal): read once by the merge kernel, they would
+    // otherwise wait dirty in L2 for the end-of-kernel write-back (measured:
+    // 16.5 -> 14.9 us at a 2048-key prefix, merge 4.0 -> 4.3 us)
+    const int Rpad = row_tiles * kTileRows;
+    const size_t bh = (size_t)b * a.Hkv + hk;  // the merge reads (request, kv-head)
+    const size_t nbh = (size_t)a.batch * a.Hkv;
+    if (row_valid) {  // rows past num_nodes are zeroed by the merge, which never reads them
+      float* po = part_o + (((size_t)z * nbh + bh) * Rpad + row) * kD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          floatx4 v4 = {acc_o[db][4 * j], acc_o[db][4 * j + 1], acc_o[db][4 * j + 2],
+                        acc_o[db][4 * j + 3]};
+          __builtin_nontemporal_store(v4, reinterpret_cast<floatx4*>(po + 32 * db + 8 * j + 4 * gq));
+        }
+      if (gq == 0) {
+        float* pm = part_ml + (((size_t)z * nbh + bh) * Rpad + row) * 2;
+        __builtin_nontemporal_store(m_run, pm);
+        __builtin_nontemporal_store(l_row, pm + 1);
+      }
+    }
+  };
+  if (vh != nullptr && P <= a.max_prefix_len)
+    rest(BoolTag<true>{});
+  else
+    rest(BoolTag<false>{});
 }
 
 // Merge of the split partials: 8 query rows of one (request, kv-head) per
@@ -795,9 +869,9 @@ int device_cus() {
   return cus[dev];
 }
 
-// Bytes of the fp16 V copy: max_prefix_len + T rows per request.
+// Bytes of the fp16 V copy: vh_tiles key tiles per (request, kv-head).
 size_t vh_bytes(int batch, int T, int Hkv, int max_prefix_len) {
-  return (size_t)batch * ((size_t)max_prefix_len + T) * Hkv * kD * 2;
+  return (size_t)batch * Hkv * (size_t)vh_tiles(T, max_prefix_len) * kTileBytes;
 }
 
 // Split of each row tile's key range across workgroups: pick the count that
@@ -841,7 +915,7 @@ AttnSplit plan_split(int dtype, int batch, int T, int Hq, int Hkv, int D, int ma
   }
   s.units = (int)units;
   s.per_xcd = (int)(per_unit8 * s.chunk * s.row_tiles);
-  s.preconv = (s.row_tiles >= kPreconvMinRowTiles && batch <= 65535 &&
+  s.preconv = (s.row_tiles >= kPreconvMinRowTiles && batch <= 65535 && Hkv <= 65535 &&
                vh_bytes(batch, T, Hkv, max_prefix_len) <= kPreconvMaxBytes)
                   ? 1
                   : 0;
@@ -898,9 +972,8 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   uint16_t* vh = nullptr;
   if (s.preconv) {
     vh = reinterpret_cast<uint16_t*>(p);
-    const int64_t vecs = ((int64_t)a.max_prefix_len + a.T) * a.Hkv * (kD / 8);
-    hipLaunchKernelGGL(k_v_f16, dim3((unsigned)((vecs + 2047) / 2048), a.batch), dim3(256), 0, st,
-                       a, vh);
+    hipLaunchKernelGGL(k_v_f16, dim3((unsigned)vh_tiles(a.T, a.max_prefix_len), a.Hkv, a.batch),
+                       dim3(256), 0, st, a, vh);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

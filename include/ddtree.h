@@ -181,9 +181,10 @@ int ddtree_mask(const int32_t *parents, const int32_t *num_nodes, int batch, int
  *   workspace     >= ddtree_verify_workspace_size(...) bytes: the split-key
  *                 partials, and (bf16, when 16 or more 128-row tiles per
  *                 (request, kv-head) would each convert the same V tiles)
- *                 an fp16 copy of the V rows read, batch * (max_prefix_len
- *                 + T) rows; a request with P_b > max_prefix_len converts
- *                 its own tiles instead (same values)
+ *                 an fp16 copy of the V key tiles read, batch * Hkv *
+ *                 (ceil(max_prefix_len / 64) + ceil(T / 64)) tiles of 64
+ *                 keys x 128 dims; a request with P_b > max_prefix_len
+ *                 converts its own tiles instead (same values)
  *
  * Request b's rows are checked on the device (the offsets and lengths may
  * come from earlier kernels): kv_offsets[b] >= 0, P_b >= 0 and

@@ -21,6 +21,9 @@ kernel, every row of one query head per (request, kv-head) where the
 oracle's cost allows it (all but the 65,536-key workload, which compares
 every row of one head for one kv-head per request), and each request's
 first, last and padding rows.
+The fp16 V copy (many row tiles per (request, kv-head)) runs on full trees
+and on cut trees whose dropped nodes' K/V rows hold NaN, beside a request
+whose prefix exceeds max_prefix_len (it converts its own tiles).
 Device-side checks: V values beyond the fp16 range and requests whose K/V
 rows are outside the caches are reported in the status words.
 """
@@ -217,7 +220,8 @@ def test_attn_bf16_preconverted_v():
     tree = _tree(B, L, V, K, N, seed=513)
     q, k, v = _qkv(B, T, Hq, Hkv, P, seed=513)
     ws_pre = api.ddtree_verify_workspace_size(0, B, T, Hq, Hkv, 128, max_prefix)
-    assert ws_pre >= B * (max_prefix + T) * Hkv * 128 * 2      # the fp16 copy is planned
+    tiles = -(-max_prefix // 64) + -(-T // 64)
+    assert ws_pre >= B * Hkv * tiles * 64 * 128 * 2      # the fp16 copy is planned
     offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
     total = k.shape[0]
     offs_bad = offs.clone()
@@ -232,6 +236,43 @@ def test_attn_bf16_preconverted_v():
     check_attn(out, _ref(q, k, v, offs2, P, tree, T, sel), sel, torch.bfloat16)
     assert torch.all(out[1] == 0)
     assert st.tolist() == [0, 8, 0], st
+
+
+def test_attn_bf16_preconverted_v_cut_trees():
+    """The fp16 V pass on cut trees: 33 row tiles (T = 513, g = 8), a prefix
+    that fills its key tiles exactly, a tree-only request, and a ragged
+    prefix. Requests 0 and 2 keep 300 and 65 of their nodes, and the K/V
+    rows of the dropped nodes hold NaN: no kernel may read them (the pass
+    writes zeros for keys a tile does not hold). Every row of one query head
+    per kv-head, and each request's rows around num_nodes for every head."""
+    B, L, V, K, N, Hq, Hkv = 3, 6, 60, 6, 512, 64, 8
+    T = N + 1
+    P = [640, 0, 1333]
+    max_prefix = 1400
+    tree = _tree(B, L, V, K, N, seed=514)
+    cut = {0: 300, 2: 65}
+    for b, n in cut.items():
+        tree["num_nodes"][b] = n
+        tree["mask"][b, n:] = 0
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=514)
+    offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
+    for b, n in cut.items():
+        o = int(offs[b]) + P[b]
+        k[o + n:o + T] = float("nan")
+        v[o + n:o + T] = float("nan")
+    note("attn bf16 preconverted V, cut trees P=%s max_prefix=%d" % (P, max_prefix))
+    out, offs2, st = _run(q, k, v, P, tree, T, max_prefix=max_prefix, offs=offs)
+    g = Hq // Hkv
+    heads = [hk * g + (hk * 5 + 1) % g for hk in range(Hkv)]
+    sel = [(b, i, h) for b in range(B) for i in range(T) for h in heads]
+    for b in range(B):
+        n = int(tree["num_nodes"][b])
+        sel += [(b, i, h) for i in range(max(n - 2, 0), min(n + 2, T)) for h in range(Hq)]
+    sel = sorted(set(sel))
+    check_attn(out, _ref(q, k, v, offs2, P, tree, T, sel), sel, torch.bfloat16)
+    for b, n in cut.items():
+        assert torch.all(out[b, n:] == 0)
+    assert np.all(st == 0), st
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
