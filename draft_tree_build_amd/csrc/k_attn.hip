@@ -12,18 +12,18 @@
 // one (request, kv-head) -- rows are node-major, the g = Hq/Hkv query heads
 // of a node adjacent, so GQA shares every K/V tile across g heads. Key tiles
 // of 64 rows go from HBM straight into LDS by DMA (global_load_lds, no
-// registers), row-major with an XOR swizzle of the 16-byte chunks; V
-// fragments come out transposed through ds_read_b64_tr_b16. Per wave and
-// tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
+// registers), row-major with an XOR swizzle of the 16-byte chunks. Per wave
+// and tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16
 // (lane = query row), online softmax in fp32 (exp2 domain) against a
 // running reference that moves only when the weights would leave the fp16
-// range, O^T += V^T P^T on v_mfma_f32_32x32x16_f16: each V tile is converted
-// to fp16 in LDS once (every wave converts the rows it staged) -- or, when
-// many row tiles read every V tile, a pass of its own (k_v_f16) converts the
-// request's V tiles once before the main kernel and stores them in the order
-// the MFMA operands are read, so that the main kernel copies each tile as
-// one block and reads a V fragment with one 16-byte load -- and P enters as
-// fp16 (2^-11 relative per weight, against 2^-8 for bf16 weights). A row tile of
+// range, O^T += V^T P^T on v_mfma_f32_32x32x16_f16 with P as fp16 (2^-11
+// relative per weight, against 2^-8 for bf16 weights). V enters as fp16 in
+// fragment order -- each MFMA operand fragment one 16-byte load per lane:
+// every wave converts the V rows it staged once, taking them out transposed
+// through ds_read_b64_tr_b16 and writing them back in that order, or, when
+// many row tiles read every V tile, a pass of its own (k_v_f16) writes the
+// request's V tiles so once before the main kernel, which then copies each
+// tile as one block. A row tile of
 // at most 32 rows has two waves take its keys by 32-key halves. The key tile
 // list is prefix tiles then tree tiles (mask applied); long lists are split
 // across workgroups and merged by a second kernel (log-sum-exp weights).
@@ -49,7 +49,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // row bits with their two pairs swapped. Measured on gfx950 (LDS bank
 // conflict counter), this keeps both the K fragment reads (16 keys, one
 // chunk each) and the V transpose reads (4 consecutive keys, 2 chunks each)
-// free of bank conflicts.
+// free of bank conflicts. A V tile is then rewritten in fragment order
+// (v_tile_to_frag).
 constexpr int kTileBytes = kKeys * kD * 2;  // 16 KB
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
@@ -79,27 +80,34 @@ __device__ __forceinline__ halfx8 v_frag_tr(const unsigned char* p0, const unsig
   return __builtin_bit_cast(halfx8, (short8){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
 }
 
-// bf16 -> fp16 in place for the four 1 KB blocks of a V tile that wave w
-// staged (bytes 4096 w .. 4096 w + 4095; 16 bytes per lane and block). The
-// conversion is exact for |v| in [2^-14, 65504]; smaller values round to
-// fp16 subnormals (absolute error <= 2^-25). Called after the wave's own
-// DMA has landed and before the barrier that publishes the tile.
-__device__ __forceinline__ void v_tile_to_f16(unsigned char* vbuf, int w, int lane) {
-  // all four reads first: one LDS round trip instead of four
-  uint4 u[4];
+// bf16 -> fp16 for key step s = w of a V tile -- the 16 rows that wave w
+// staged, bytes 4096 w .. 4096 w + 4095, row-major -- rewritten in place in
+// fragment order: the fragment of dims 32 db .. + 31 at (4 w + db) * 1024,
+// lane l's 16 bytes at 16 l (the layout k_v_f16 writes). The conversion is
+// exact for |v| in [2^-14, 65504]; smaller values round to fp16 subnormals
+// (absolute error <= 2^-25). Called after the wave's own DMA has landed and
+// before the barrier that publishes the tile. vtr[db][rd] = v_tr_off(lane,
+// db, rd).
+__device__ __forceinline__ void v_tile_to_frag(unsigned char* vbuf, int w, int lane, const int (&vtr)[4][2]) {
+  const unsigned char* rows = vbuf + w * 16 * 256;
+  halfx8 f[4];  // bf16 bit patterns
 #pragma unroll
-  for (int j = 0; j < 4; ++j) u[j] = *reinterpret_cast<const uint4*>(vbuf + (4 * w + j) * 1024 + 16 * lane);
+  for (int db = 0; db < 4; ++db) f[db] = v_frag_tr(rows + vtr[db][0], rows + vtr[db][1]);
+  // every read of the wave before any write: the writes cover rows that
+  // other lanes read
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t in[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+  for (int db = 0; db < 4; ++db) {
+    const uint4 u = __builtin_bit_cast(uint4, f[db]);
+    const uint32_t in[4] = {u.x, u.y, u.z, u.w};
     uint32_t o[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const floatx2 f = {__uint_as_float(in[q] << 16), __uint_as_float(in[q] & 0xFFFF0000u)};
-      o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, halfx2));
+      const floatx2 x = {__uint_as_float(in[q] << 16), __uint_as_float(in[q] & 0xFFFF0000u)};
+      o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, halfx2));
     }
-    *reinterpret_cast<uint4*>(vbuf + (4 * w + j) * 1024 + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(vbuf + (4 * w + db) * 1024 + 16 * lane) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -140,7 +148,7 @@ __host__ __device__ inline int vh_tiles(int T, int max_prefix_len) {
 }
 
 // fp16 copy of the V tiles the verify reads, with the same rounding as
-// v_tile_to_f16, laid out in fragment order: key tile t of (request b,
+// v_tile_to_frag, laid out in fragment order: key tile t of (request b,
 // kv-head h) is 16 KB at vh + ((b * Hkv + h) * vh_tiles + t) * 16384 bytes
 // -- t numbers the tiles as the main kernel does (prefix tiles, then tree
 // tiles from key P_b on) -- and holds the 16 V fragments of the tile, key
@@ -394,7 +402,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
     int kfrag[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kfrag[ks] = tile_off(pi_m, 2 * ks + gq);
-    // V fragments from a row-major tile (key step 0; see v_tr_off)
+    // V fragments from a row-major tile (key step 0; see v_tr_off), for the
+    // in-kernel conversion
     int vfrag[4][2];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -407,20 +416,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
       return (t >= np && row_valid) ? mrow[t - np] : 0ull;
     };
     // V fragments (A operand of O^T += V^T P^T) of 32-key half kb of the tile
-    // in vl: key steps s = 2 kb + hf, one 16-byte read each from a tile in
-    // fragment order, two transposed reads from a row-major one
+    // in vl, which is in fragment order: key steps s = 2 kb + hf, one
+    // 16-byte read each
     auto read_v = [&](const unsigned char* vl, int kb, halfx8 (&vf)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          if (pre) {
-            vf[db][hf] = *reinterpret_cast<const halfx8*>(vl + (4 * (2 * kb + hf) + db) * 1024 + 16 * lane);
-          } else {
-            const int kofs = (32 * kb + 16 * hf) * 256;
-            vf[db][hf] = v_frag_tr(vl + vfrag[db][0] + kofs, vl + vfrag[db][1] + kofs);
-          }
-        }
+        for (int hf = 0; hf < 2; ++hf)
+          vf[db][hf] = *reinterpret_cast<const halfx8*>(vl + (4 * (2 * kb + hf) + db) * 1024 + 16 * lane);
     };
     // Scores of 32-key half kb masked to the allowed keys (tree tiles and the
     // ragged last prefix tile). Query rows past num_nodes need no masking:
@@ -601,21 +604,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, 
         mword_next = load_mword(t_begin);
       }
       __builtin_amdgcn_s_waitcnt(0);
-      if (t_begin < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
+      if (t_begin < t_end && !pre) v_tile_to_frag(v_lds0, w, lane, vfrag);
       __syncthreads();
       for (int t = t_begin; t < t_end; t += 2) {
         {
           const uint64_t mword = mword_next;
           body(t, mword, k_lds0, v_lds0, k_lds1, v_lds1, t + 1 < t_end);
           __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of tile t+1 has landed
-          if (t + 1 < t_end && !pre) v_tile_to_f16(v_lds1, w, lane);
+          if (t + 1 < t_end && !pre) v_tile_to_frag(v_lds1, w, lane, vfrag);
           __syncthreads();
         }
         if (t + 1 < t_end) {
           const uint64_t mword = mword_next;
           body(t + 1, mword, k_lds1, v_lds1, k_lds0, v_lds0, t + 2 < t_end);
           __builtin_amdgcn_s_waitcnt(0);
-          if (t + 2 < t_end && !pre) v_tile_to_f16(v_lds0, w, lane);
+          if (t + 2 < t_end && !pre) v_tile_to_frag(v_lds0, w, lane, vfrag);
           __syncthreads();
         }
       }
