@@ -34,6 +34,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 import types
@@ -90,10 +91,15 @@ def algorithmic_work(w, prefix_lens, num_nodes, depths, esize, moved_rows=0):
 
 
 def source_hash(rels):
+    """Hash of the code of the given sources: comments and whitespace are
+    removed first, so that an edit of the text alone keeps the counters."""
     h = hashlib.sha256()
     for rel in rels:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            code = f.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -229,8 +229,8 @@ struct BoolTag {
 // its Q rows, and every request is spread over the XCDs, which keeps them
 // evenly loaded when prefix lengths differ. Splits are cut into several
 // units only when there are fewer (request, kv-head) pairs than XCDs. Key
-// tiles are double-buffered in LDS: tile t+1 is fetched into registers while
-// tile t is computed.
+// tiles are double-buffered in LDS: tile t+1 is copied into the other buffer
+// while tile t is computed.
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, AttnSplit pl, float* part_o,
                                                       float* part_ml, const uint16_t* vh) {
   // two buffers of K and V tiles; 64 KB
