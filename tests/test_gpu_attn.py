@@ -23,7 +23,10 @@ every row of one head for one kv-head per request), and each request's
 first, last and padding rows.
 The fp16 V copy (many row tiles per (request, kv-head)) runs on full trees
 and on cut trees whose dropped nodes' K/V rows hold NaN, beside a request
-whose prefix exceeds max_prefix_len (it converts its own tiles).
+whose prefix exceeds max_prefix_len (it converts its own tiles). Twelve
+seeded random shapes (1-4 requests, GQA groups 1-8, budgets up to 399,
+prefixes up to 2,500 keys, some above max_prefix_len, trees cut at random
+with NaN in the dropped rows) cross the split, V-pass and last-tile cases.
 Device-side checks: V values beyond the fp16 range and requests whose K/V
 rows are outside the caches are reported in the status words.
 """
@@ -272,6 +275,69 @@ def test_attn_bf16_preconverted_v_cut_trees():
     check_attn(out, _ref(q, k, v, offs2, P, tree, T, sel), sel, torch.bfloat16)
     for b, n in cut.items():
         assert torch.all(out[b, n:] == 0)
+    assert np.all(st == 0), st
+
+
+def _random_case(seed):
+    """One seeded shape: 1-4 requests, GQA group 1-8, a tree budget and
+    prefixes that may or may not split keys or reach the fp16 V pass, a
+    max_prefix_len that some prefixes may exceed, and trees cut at random
+    with NaN in the K/V rows of the dropped nodes."""
+    rng = np.random.default_rng(seed)
+    big = seed % 3 == 0           # 17 or more row tiles: the fp16 V pass
+    B = int(rng.integers(1, 5))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = 8 if big else int(rng.choice([1, 2, 4, 8]))
+    N = int(rng.integers(256, 400)) if big else int(rng.integers(1, 400))
+    L = int(rng.integers(2, 9))
+    K = int(rng.integers(2, 7))
+    P = [int(x) for x in rng.integers(0, 2500, size=B)]
+    mp = max(P)
+    if rng.random() < 0.4 and mp > 64:
+        mp = int(rng.integers(mp // 2, mp))       # some prefixes exceed it
+    cuts = {b: int(rng.integers(0, N + 2)) for b in range(B) if rng.random() < 0.4}
+    return dict(B=B, Hkv=Hkv, Hq=Hkv * g, N=N, L=L, K=K, P=P, max_prefix=mp, cuts=cuts)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attn_bf16_random_shapes(seed):
+    """Seeded random shapes across the plan's branches (splits, the fp16 V
+    pass and its fallback, last row tiles of any size, cut trees): every row
+    of one query head per (request, kv-head), every head of each request's
+    rows around num_nodes, and 256 random rows."""
+    c = _random_case(1000 + seed)
+    B, Hq, Hkv, N, P = c["B"], c["Hq"], c["Hkv"], c["N"], c["P"]
+    T = N + 1
+    tree = _tree(B, c["L"], 40, c["K"], N, seed=2000 + seed)
+    for b, n in c["cuts"].items():
+        n = min(n, int(tree["num_nodes"][b]))
+        tree["num_nodes"][b] = n
+        tree["mask"][b, n:] = 0
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=3000 + seed)
+    offs = synth.kv_offsets(torch.as_tensor(P, dtype=torch.int32), T)
+    for b in range(B):
+        n = int(tree["num_nodes"][b])
+        o = int(offs[b]) + P[b]
+        k[o + n:o + T] = float("nan")
+        v[o + n:o + T] = float("nan")
+    note("attn bf16 random seed=%d B=%d T=%d Hq=%d Hkv=%d P=%s max_prefix=%d num_nodes=%s" % (
+        seed, B, T, Hq, Hkv, P, c["max_prefix"], list(tree["num_nodes"])))
+    out, offs2, st = _run(q, k, v, P, tree, T, max_prefix=c["max_prefix"], offs=offs)
+    g = Hq // Hkv
+    rng = np.random.default_rng(seed)
+    sel = set()
+    for b in range(B):
+        for hk in range(Hkv):
+            h = hk * g + int(rng.integers(g))
+            sel.update((b, i, h) for i in range(T))
+        n = int(tree["num_nodes"][b])
+        sel.update((b, i, h) for i in range(max(n - 2, 0), min(n + 2, T)) for h in range(Hq))
+    for _ in range(256):
+        sel.add((int(rng.integers(B)), int(rng.integers(T)), int(rng.integers(Hq))))
+    sel = sorted(sel)
+    check_attn(out, _ref(q, k, v, offs2, P, tree, T, sel), sel, torch.bfloat16)
+    for b in range(B):
+        assert torch.all(out[b, int(tree["num_nodes"][b]):] == 0)
     assert np.all(st == 0), st
 
 
