@@ -4,7 +4,8 @@ Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees",
 §3, §4.1-4.3, App. A. Covers every kernel variant (register-resident rows of
 several lengths, streaming rows, unaligned rows), temperature 1 / scaled / 0,
 the exact fallback of the top-K selection, non-finite and all -inf rows,
-budget and block limits, and the full-size workloads.
+budget and block limits, the full-size workloads, and sixteen seeded random
+shapes across the row-kernel variants, the heap and the level selection.
 """
 import numpy as np
 import pytest
@@ -286,3 +287,32 @@ def test_build_level_selection_degenerate_rows(value):
         g, _ = gpu_build(x, [1, 2], K, N, tau)
         o = oracle.build_tree(x, [1, 2], K, N, tau)
         assert_same_build(g, o)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_build_random_shapes(seed):
+    """Seeded random shapes: 1-8 requests, block sizes 1-32, vocabularies
+    from 2 to 200,000 (every row-kernel variant, aligned or not), K up to 32,
+    budgets up to 1,024 (the heap and the level selection on either side of
+    their switch), draft temperatures 0, 1 and others, bf16 or f32 logits,
+    some rows quantised to force ties."""
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 9))
+    L = int(rng.integers(1, 33))
+    V = int(rng.choice([int(rng.integers(2, 300)), int(rng.integers(300, 20000)),
+                        int(rng.integers(20000, 200000))]))
+    K = int(rng.integers(1, min(32, V) + 1))
+    N = int(rng.choice([int(rng.integers(1, 72)), int(rng.integers(72, 160)),
+                        int(rng.integers(160, 1025))]))
+    tau = float(rng.choice([0.0, 1.0, float(rng.uniform(0.3, 2.0))]))
+    dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+    x = _logits(B, L, V, seed=600 + seed, sigma=float(rng.uniform(0.5, 4.0)), dtype=torch.float32,
+                boost=float(rng.choice([0.0, 8.0])))
+    if rng.random() < 0.3:
+        x = torch.round(x)                         # ties
+    x = x.to(dtype)
+    roots = torch.as_tensor(rng.integers(0, V, size=B), dtype=torch.int32)
+    note("build random seed=%d B=%d L=%d V=%d K=%d N=%d tau=%g %s" % (seed, B, L, V, K, N, tau, dtype))
+    g, _ = gpu_build(x, roots, K, N, tau)
+    o = oracle.build_tree(x, roots, K, N, tau)
+    assert_same_build(g, o)
