@@ -3,6 +3,9 @@
 Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees",
 §4.1: walk with the target's decoding rule (argmax at temperature 0); the
 matched path is accepted, the first unmatched target token is the bonus.
+Besides the targeted cases, twelve seeded random shapes (requests, block
+size, budget, vocabulary, dtype, share of nodes whose target follows a
+child) are compared bit for bit.
 """
 import numpy as np
 import pytest
@@ -127,3 +130,43 @@ def test_accept_optional_outputs_absent():
     np.testing.assert_array_equal(alen.cpu().numpy(), o["accept_len"])
     np.testing.assert_array_equal(bonus.cpu().numpy(), o["bonus"])
     assert o["accept_len"].max() >= 2
+
+
+def _random_accept_case(seed):
+    """A seeded shape for the acceptance tests: 1-8 requests, blocks of 1-32
+    positions, budgets up to 1,024, vocabularies up to 200,000 (fewer when the
+    target logits would pass 1e8 values), bf16 or f32, and target logits whose
+    top token follows one child's token at a random share of the nodes."""
+    rng = np.random.default_rng(700 + seed)
+    B = int(rng.integers(1, 9))
+    L = int(rng.integers(1, 33))
+    N = int(rng.choice([int(rng.integers(1, 72)), int(rng.integers(72, 300)),
+                        int(rng.integers(300, 1025))]))
+    V = int(rng.choice([int(rng.integers(2, 300)), int(rng.integers(300, 20000)),
+                        int(rng.integers(20000, 200000))]))
+    V = max(2, min(V, int(1e8) // (B * (N + 1))))
+    K = int(rng.integers(1, min(32, V) + 1))
+    dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+    g = torch.Generator().manual_seed(800 + seed)
+    roots = [int(r) for r in rng.integers(0, V, size=B)]
+    tree = oracle.build_tree(torch.randn(B, L, V, generator=g) * 2, roots, K, N, 1.0)
+    T = N + 1
+    x = torch.from_numpy(rng.standard_normal((B, T, V)).astype(np.float32))
+    follow = float(rng.uniform(0.3, 1.0))
+    for b in range(B):
+        n = int(tree["num_nodes"][b])
+        par = tree["parents"][b, 1:n]
+        for i in np.unique(par):
+            if rng.random() < follow:
+                kids = np.nonzero(par == i)[0] + 1
+                x[b, i, int(tree["tokens"][b, kids[int(rng.integers(len(kids)))]])] += 9.0
+    return tree, x.to(dtype), L, dict(B=B, L=L, V=V, K=K, N=N, dtype=dtype)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_accept_random_shapes(seed):
+    tree, tl, L, c = _random_accept_case(seed)
+    note("accept random seed=%d %s" % (seed, c))
+    g = _gpu_accept(tl, None, tree, L)
+    o = oracle.accept(tl, None, tree["tokens"], tree["parents"], tree["num_nodes"], L)
+    _same(g, o)

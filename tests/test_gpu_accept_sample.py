@@ -4,7 +4,9 @@ Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees",
 §4.1: the tree is walked with the target's own decoding rule; at temperature
 > 0 that rule draws from the target's softmax. Both sides draw with
 Philox4x32-10 on the same counter and key and an integer CDF, so the sampled
-tokens, and the walk that follows them, agree exactly.
+tokens, and the walk that follows them, agree exactly. Twelve seeded random
+shapes (those of the greedy acceptance test) run at random temperatures,
+seeds and offsets.
 """
 import numpy as np
 import pytest
@@ -180,3 +182,20 @@ def test_accept_sample_overflowing_products(dtype):
         o = oracle.accept_sample(tl, tree["tokens"], tree["parents"], tree["num_nodes"], L, tau,
                                  5, 2)
         _same(g, o)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_accept_sample_random_shapes(seed):
+    """Seeded random shapes (those of the greedy acceptance test), a random
+    target temperature in [0.3, 2] and random seed and offset words."""
+    from test_gpu_accept import _random_accept_case
+    tree, tl, L, c = _random_accept_case(seed)
+    rng = np.random.default_rng(950 + seed)
+    tau = float(rng.uniform(0.3, 2.0))
+    key = int(rng.integers(0, 2**63))
+    offset = int(rng.integers(0, 2**40))
+    note("accept_sample random seed=%d tau=%g %s" % (seed, tau, c))
+    g = _gpu_sample(tl, tree, L, tau, seed=key, offset=offset)
+    o = oracle.accept_sample(tl, tree["tokens"], tree["parents"], tree["num_nodes"], L, tau, key,
+                             offset)
+    _same(g, o)
