@@ -5,7 +5,8 @@ Page: "Accelerating Speculative Decoding with Block Diffusion Draft Trees",
 the next root. Covers bf16 and f32 caches, head slices from 64 to 1024 bytes,
 one to eight kv-heads, paths that skip first children (sources that are other
 moves' destinations), full-depth paths of 64 nodes, empty acceptance,
-malformed requests next to good ones, and the full-size workload shapes.
+malformed requests next to good ones, the full-size workload shapes, and
+twelve seeded random shapes.
 """
 import numpy as np
 import pytest
@@ -158,3 +159,30 @@ def test_commit_full_size_workloads(name):
     acc = oracle.accept(None, ids, tree["tokens"], tree["parents"], tree["num_nodes"], w.L)
     note("commit workload %s (%d rows, accepted %s)" % (name, rows, list(acc["accept_len"][:8])))
     _check(k, v, offs.numpy(), P.numpy(), acc, w.T)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_commit_random_shapes(seed):
+    """Seeded random shapes: 1-8 requests, blocks of 1-32 positions, budgets
+    up to 1,024, 1-8 kv-heads, head slices of 16 to 1,024 bytes in bf16 or
+    f32, prefixes of 0-500 rows, and walks that follow the tree at a random
+    rate (empty acceptance included)."""
+    rng = np.random.default_rng(1100 + seed)
+    B = int(rng.integers(1, 9))
+    L = int(rng.integers(1, 33))
+    N = int(rng.choice([int(rng.integers(1, 72)), int(rng.integers(72, 1025))]))
+    K = int(rng.integers(1, 9))
+    Hkv = int(rng.integers(1, 9))
+    dtype = torch.float32 if rng.random() < 0.4 else torch.bfloat16
+    per16 = 4 if dtype == torch.float32 else 8          # values per 16 bytes
+    D = per16 * int(rng.integers(1, 65))
+    P = [int(x) for x in rng.integers(0, 501, size=B)]
+    g = torch.Generator().manual_seed(1200 + seed)
+    tree = oracle.build_tree(torch.randn(B, L, 50, generator=g) * 2, list(range(B)), K, N, 1.0)
+    T = N + 1
+    k, v, offs, rng2 = _region_caches(P, T, Hkv, D, dtype, seed=1300 + seed)
+    ids = _walk_ids(tree, rng2, follow=float(rng.uniform(0.0, 1.0)))
+    acc = oracle.accept(None, ids, tree["tokens"], tree["parents"], tree["num_nodes"], L)
+    note("commit random seed=%d B=%d L=%d N=%d Hkv=%d D=%d %s lens=%s" % (
+        seed, B, L, N, Hkv, D, dtype, list(acc["accept_len"])))
+    _check(k, v, offs, P, acc, T)
