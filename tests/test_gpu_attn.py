@@ -27,6 +27,8 @@ whose prefix exceeds max_prefix_len (it converts its own tiles). Twelve
 seeded random shapes (1-4 requests, GQA groups 1-8, budgets up to 399,
 prefixes up to 2,500 keys, some above max_prefix_len, trees cut at random
 with NaN in the dropped rows) cross the split, V-pass and last-tile cases.
+Root-only trees (T = 1) are single-query decode attention; with no prefix
+the output is the root's own V row, exactly.
 Device-side checks: V values beyond the fp16 range and requests whose K/V
 rows are outside the caches are reported in the status words.
 """
@@ -297,6 +299,28 @@ def _random_case(seed):
         mp = int(rng.integers(mp // 2, mp))       # some prefixes exceed it
     cuts = {b: int(rng.integers(0, N + 2)) for b in range(B) if rng.random() < 0.4}
     return dict(B=B, Hkv=Hkv, Hq=Hkv * g, N=N, L=L, K=K, P=P, max_prefix=mp, cuts=cuts)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (64, 8)])
+def test_attn_root_only_trees(Hq, Hkv, dtype):
+    """T = 1 (no drafted node): single-query decode attention over the prefix
+    and the root itself, with prefixes of 0, 1, 63 and 4,100 keys (split
+    keys); with no prefix the output is the root's own V row."""
+    B, T, P = 4, 1, [0, 1, 63, 4100]
+    tree = dict(num_nodes=np.ones(B, np.int32), mask=np.ones((B, 1, 1), np.uint64))
+    q, k, v = _qkv(B, T, Hq, Hkv, P, seed=Hq + Hkv, dtype=dtype, D=128)
+    note("attn root-only Hq=%d Hkv=%d %s" % (Hq, Hkv, dtype))
+    out, offs, st = _run(q, k, v, P, tree, T)
+    sel = _all_rows(B, T, Hq)
+    check_attn(out, _ref(q, k, v, offs, P, tree, T, sel), sel, dtype)
+    g = Hq // Hkv
+    root = int(offs[0]) + P[0]
+    want = v[root].float().repeat_interleave(g, dim=0)          # [Hq, D]
+    # one key of weight exactly 1: V itself (bf16 V passes fp16 and back
+    # unchanged outside the fp16 subnormal range)
+    assert torch.allclose(out[0, 0].float(), want, atol=1e-6, rtol=0)
+    assert np.all(st == 0), st
 
 
 @pytest.mark.parametrize("seed", range(12))
