@@ -567,6 +567,13 @@ void oracle_accept(const void *target_logits, int dtype, const int32_t *target_i
 /* the first v whose running sum of u exceeds theta = floor(r * S / 2^64).  */
 /* Token v is then drawn with probability u_v / S. A row without a finite   */
 /* value (S = 0) gives token 0.                                             */
+/*                                                                          */
+/* Parity unpinned for the draw's convention: the pages fix no generator,   */
+/* and the word order of r, the counter layout and the strict "exceeds"     */
+/* are this implementation's choices. The pins fix the law of the draw      */
+/* (chi-square against softmax, exact special cases), Philox itself (the    */
+/* published known-answer vectors) and the counter's independence; the same */
+/* convention changed on both sides would still pass them.                  */
 /* ------------------------------------------------------------------------ */
 static void philox_round(uint32_t c[4], const uint32_t k[2])
 {
