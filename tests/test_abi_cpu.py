@@ -45,6 +45,19 @@ def test_version_strerror_and_sizes():
     assert dtb.ddtree_verify_workspace_size(0, 1, 65, 30, 8, 128, 2048) == 0  # Hq % Hkv
 
 
+def test_verify_workspace_v_copy_threshold():
+    """The bf16 verify plans its fp16 V copy from 16 row tiles of 128 query
+    rows per (request, kv-head): one request, one kv-head, 8 query heads and
+    a 100-key prefix (6 key tiles, too few to split) give 15 row tiles at
+    T = 240 (no copy: the minimum workspace) and 16 at T = 241, where the
+    copy holds ceil(100/64) + ceil(241/64) = 6 tiles of 64 x 128 fp16 values.
+    Two requests and two kv-heads hold four times as many."""
+    assert dtb.ddtree_verify_workspace_size(0, 1, 240, 8, 1, 128, 100) == 256
+    assert dtb.ddtree_verify_workspace_size(0, 1, 241, 8, 1, 128, 100) == 6 * 64 * 128 * 2
+    assert dtb.ddtree_verify_workspace_size(0, 2, 241, 16, 2, 128, 100) == 4 * 6 * 64 * 128 * 2
+    assert dtb.ddtree_verify_workspace_size(1, 1, 241, 8, 1, 128, 100) == 256   # f32: no copy
+
+
 # Host validation. Pointers are fake non-null addresses: every case below has
 # exactly one invalid field and must be rejected before any HIP call.
 P = ctypes.c_void_p(0x1000)
