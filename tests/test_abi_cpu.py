@@ -58,6 +58,26 @@ def test_verify_workspace_v_copy_threshold():
     assert dtb.ddtree_verify_workspace_size(1, 1, 241, 8, 1, 128, 100) == 256   # f32: no copy
 
 
+@pytest.mark.parametrize("batch,T,Hq,max_prefix,nsplit,row_tiles,v_copy", [
+    (4, 513, 64, 65536, 5, 33, True),       # B4_L32_V151936_K16_N512_P65536
+    (32, 129, 32, 16384, 2, 5, False),      # B32_L16_V151936_K8_N128_P512-16384
+    (1, 257, 32, 8192, 7, 9, False),        # L16_V151936_K16_N256_P8192
+    (1, 65, 32, 2048, 7, 3, False),         # L16_V32000_K8_N64_P2048
+])
+def test_verify_split_plan_at_benchmark_shapes(batch, T, Hq, max_prefix, nsplit, row_tiles, v_copy):
+    """The key splits the planner picks at the benchmark shapes (8 kv-heads)
+    -- the counts a sweep of 1 to 12 splits measured best or within 1% of
+    it -- read back from the workspace size: fp32 partial O and (m, l) per
+    split, row and kv-head, plus the fp16 V copy where it is planned."""
+    Hkv = 8
+    rows = nsplit * batch * Hkv * row_tiles * 128
+    align = lambda x: (x + 255) // 256 * 256
+    want = align(rows * 128 * 4) + align(rows * 2 * 4)
+    if v_copy:
+        want += batch * Hkv * (-(-max_prefix // 64) + -(-T // 64)) * 64 * 128 * 2
+    assert dtb.ddtree_verify_workspace_size(0, batch, T, Hq, Hkv, 128, max_prefix) == want
+
+
 # Host validation. Pointers are fake non-null addresses: every case below has
 # exactly one invalid field and must be rejected before any HIP call.
 P = ctypes.c_void_p(0x1000)
